@@ -1,0 +1,283 @@
+"""Pins for the float64 attention oracle (CPU only).
+
+Each test ties the oracle to something other than itself: torch's float64
+scaled_dot_product_attention (a library routine), closed forms computed by
+hand, brute force, identities of the online softmax, or the error bound that
+follows from the BLASST pruning condition (notes, section 3.1.1).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import attention as A
+from oracle import masks as M
+from workloads import get_config, gen_prefill_inputs, gen_decode_sequence
+from workloads.configs import DecodeWorkload, PrefillWorkload, MaskSpec, Segment, SEG_BLOCKWIN
+
+
+def _rand(shape, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape) * scale
+
+
+def _sdpa(q, k, v, **kw):
+    """torch fp64 SDPA on [H, N, d] numpy arrays."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None]
+    return F.scaled_dot_product_attention(t(q), t(k), t(v), **kw)[0].numpy()
+
+
+# ---- C-P1: dense special case equals the library routine -------------------
+
+def test_dense_equals_sdpa():
+    q, k, v = _rand((40, 16), 0), _rand((56, 16), 1), _rand((56, 8), 2)
+    scale = 1 / math.sqrt(16)
+    ours = A.masked_attention(q, k, v, np.ones((40, 56), bool), scale)
+    ref = _sdpa(q[None], k[None], v[None], scale=scale)[0]
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_causal_equals_sdpa():
+    n, d = 70, 32
+    q, k, v = _rand((n, d), 3), _rand((n, d), 4), _rand((n, d), 5)
+    allowed = np.tril(np.ones((n, n), bool))
+    ours = A.masked_attention(q, k, v, allowed, 0.2)
+    ref = _sdpa(q[None], k[None], v[None], is_causal=True, scale=0.2)[0]
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_boolean_mask_equals_sdpa():
+    n, d = 48, 16
+    q, k, v = _rand((n, d), 6), _rand((n, d), 7), _rand((n, d), 8)
+    allowed = _rand((n, n), 9) > 0.3
+    allowed[np.arange(n), np.arange(n)] = True          # SDPA returns NaN for empty rows
+    ours = A.masked_attention(q, k, v, allowed, 0.25)
+    ref = _sdpa(q[None], k[None], v[None], attn_mask=torch.from_numpy(allowed)[None], scale=0.25)[0]
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_gqa_mapping_equals_sdpa_enable_gqa():
+    """Head h must read K/V head h // (Hq/Hkv): compared with SDPA's own GQA grouping."""
+    B, N, Hq, Hkv, d = 1, 64, 8, 2, 16
+    q = torch.from_numpy(_rand((B, N, Hq, d), 10))
+    k = torch.from_numpy(_rand((B, N, Hkv, d), 11))
+    v = torch.from_numpy(_rand((B, N, Hkv, d), 12))
+    ref = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                                         is_causal=True, enable_gqa=True).transpose(1, 2)
+    for h in range(Hq):
+        for t in range(2):
+            rows, out, blocks, skip, _ = A.prefill_tile(q, k, v, 0, h, t, Br=32, Bc=16,
+                                                        scale=1 / 4, causal=True, lam=0.0, n_valid=N)
+            assert np.max(np.abs(out - ref[0, rows, h].numpy())) < 1e-12
+
+
+def test_empty_rows_are_zero():
+    q, k, v = _rand((4, 8), 13), _rand((6, 8), 14), _rand((6, 8), 15)
+    allowed = np.zeros((4, 6), bool)
+    allowed[1, 2] = True
+    out = A.masked_attention(q, k, v, allowed, 1.0)
+    assert np.all(out[[0, 2, 3]] == 0.0)
+    assert np.allclose(out[1], v[2], atol=1e-15)
+
+
+# ---- C-P2: rows of P sum to one ------------------------------------------
+
+def test_probability_rows_sum_to_one():
+    q, k, v = _rand((33, 8), 16, 3.0), _rand((77, 8), 17, 3.0), _rand((77, 8), 18)
+    allowed = _rand((33, 77), 19) > -0.5
+    _, P = A.masked_attention(q, k, v, allowed, 0.5, return_probs=True)
+    has = allowed.any(1)
+    assert np.max(np.abs(P[has].sum(1) - 1.0)) < 1e-12
+    assert np.all(P[~allowed] == 0.0)
+
+
+# ---- C-P3: diagonal-only block mask = independent per-block attention --------
+
+def test_diagonal_block_mask_equals_per_block_attention():
+    n, d, Bs = 96, 16, 32
+    spec = MaskSpec(n_valid=n, segments=(Segment(SEG_BLOCKWIN, 0, n, unit=Bs, radius=0),))
+    tm = M.tile_mask(spec, n, n, Bs, Bs)
+    assert np.array_equal(tm, np.eye(n // Bs, dtype=bool))
+    q, k, v = _rand((1, n, 1, d), 20), _rand((1, n, 1, d), 21), _rand((1, n, 1, d), 22)
+    rp, ci = M.csr_from_tile_mask(tm)
+    for t in range(n // Bs):
+        rows, out, *_ = A.prefill_tile(q, k, v, 0, 0, t, Br=Bs, Bc=Bs, scale=0.25, causal=False,
+                                       lam=0.0, n_valid=n, row_ptr=rp, col_idx=ci)
+        sl = slice(t * Bs, (t + 1) * Bs)
+        ref = _sdpa(q[0, sl, 0][None], k[0, sl, 0][None], v[0, sl, 0][None], scale=0.25)[0]
+        assert np.max(np.abs(out - ref)) < 1e-12
+
+
+# ---- C-P4: Algorithm 1 at lambda = 0 equals the two-pass masked softmax -------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alg1_lambda0_equals_two_pass(causal):
+    N, d, Br, Bc = 200, 16, 64, 32            # ragged tail: 200 = 3*64 + 8
+    q, k, v = _rand((1, N, 2, d), 23, 2.0), _rand((1, N, 1, d), 24, 2.0), _rand((1, N, 1, d), 25)
+    spec = MaskSpec(n_valid=190, segments=(Segment(SEG_BLOCKWIN, 0, 190, unit=32, radius=2),))
+    tm = M.tile_mask(spec, N, N, Br, Bc)
+    rp, ci = M.csr_from_tile_mask(tm)
+    for h in range(2):
+        for t in range(-(-N // Br)):
+            kw = dict(Br=Br, Bc=Bc, scale=0.3, causal=causal, lam=0.0, n_valid=190, row_ptr=rp, col_idx=ci)
+            _, o1, _, skip, _ = A.prefill_tile(q, k, v, 0, h, t, **kw)
+            _, o2, *_ = A.prefill_tile(q, k, v, 0, h, t, method="two_pass", **kw)
+            assert not skip.any()
+            assert np.max(np.abs(o1 - o2)) < 1e-12
+    # and the expanded token mask gives the same output through the plain definition
+    Mtok = M.expand_token_mask(tm, N, N, Br, Bc, 190, causal)
+    ref = A.masked_attention(q[0, :, 0], k[0, :, 0], v[0, :, 0], Mtok, 0.3)
+    for t in range(-(-N // Br)):
+        rows, o1, *_ = A.prefill_tile(q, k, v, 0, 0, t, Br=Br, Bc=Bc, scale=0.3, causal=causal,
+                                      lam=0.0, n_valid=190, row_ptr=rp, col_idx=ci)
+        assert np.max(np.abs(o1 - ref[rows])) < 1e-12
+
+
+# ---- closed-form worked example of the skip rule ---------------------------
+
+def test_skip_rule_closed_form_example():
+    """Keys of block j all equal (a_j, 0); q = (1, 0); scale 1; lambda = e^-2.
+    Running max / decision by hand: a = [0, -10, 1, -0.5, -1.01, 3]
+      block0 keep (first), block1 -10-0 < -2 skip, block2 keep (max->1),
+      block3 -1.5 > -2 keep, block4 -2.01 < -2 skip, block5 keep (max->3).
+    Output = sum_kept Bc e^{a_j} v_j / sum_kept Bc e^{a_j}."""
+    Bc, lam = 4, math.exp(-2.0)
+    a = np.array([0.0, -10.0, 1.0, -0.5, -1.01, 3.0])
+    k = np.zeros((len(a) * Bc, 2))
+    k[:, 0] = np.repeat(a, Bc)
+    vrow = np.arange(len(a), dtype=float) * 10.0 + 1.0
+    v = np.repeat(vrow, Bc)[:, None]
+    q = np.array([[1.0, 0.0]])
+    rows = np.array([len(a) * Bc - 1])
+    out, skip, margin = A.blasst_tile(q, k, v, rows, np.arange(len(a)), Bc, 1.0, lam, 10 ** 9, False)
+    assert skip.tolist() == [False, True, False, False, True, False]
+    kept = ~skip
+    w = np.exp(a[kept])
+    assert abs(out[0, 0] - (w * vrow[kept]).sum() / w.sum()) < 1e-12
+    assert abs(margin[1] - (-10.0 + 2.0)) < 1e-12 and abs(margin[4] - (-2.01 + 2.0)) < 1e-12
+    # decode oracle on the same data (G = 1) agrees, both forms
+    for meth in ("loop", "closed_form"):
+        o2, s2, _ = A.decode_group(q, k, v, Bc, 1.0, lam, meth)
+        assert s2.tolist() == skip.tolist()
+        assert abs(o2[0, 0] - out[0, 0]) < 1e-12
+
+
+# ---- C-P5: sequential loop skip set = cumulative-max closed form ------------
+
+def _concentrated_case(L=1024, Hq=4, Hkv=1, d=32):
+    cfg = PrefillWorkload(name="t", description="", dtype="bf16", B=1, Hq=Hq, Hkv=Hkv, N=L, d=d,
+                          Br=64, Bc=32, causal=True, lam=0.0, mask=None, seed=77, generator="concentrated")
+    return cfg, gen_prefill_inputs(cfg)
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-2, 0.1, 0.4, 0.9])
+def test_skip_loop_equals_cummax_form(lam):
+    cfg, (q, k, v) = _concentrated_case()
+    n = cfg.N
+    for h in (0, 3):
+        for t in (0, 5, 15):
+            rows, out, blocks, skip, margin = A.prefill_tile(q, k, v, 0, h, t, Br=64, Bc=32,
+                                                             scale=cfg.scale, causal=True, lam=lam, n_valid=n)
+            qr = A.as_f64(q[0, rows[0]:rows[-1] + 1, h])
+            s2, _ = A.skip_set_vectorized(qr, A.as_f64(k[0, :, 0]), rows, blocks, 32, cfg.scale, lam, n, True)
+            assert np.array_equal(skip, s2)
+
+
+# ---- C-P6: monotone in lambda, first block never skipped --------------------
+
+def test_skip_monotone_and_first_block_kept():
+    cfg, (q, k, v) = _concentrated_case()
+    prev = None
+    for lam in (0.0, 1e-6, 1e-3, 0.05, 0.3, 0.7, 0.99):
+        sets = []
+        for t in (3, 9, 15):
+            _, _, blocks, skip, _ = A.prefill_tile(q, k, v, 0, 1, t, Br=64, Bc=32, scale=cfg.scale,
+                                                   causal=True, lam=lam, n_valid=cfg.N)
+            assert not skip[0]
+            sets.append(skip)
+        cur = np.concatenate(sets)
+        if prev is not None:
+            assert np.all(cur >= prev)          # skip(l1) subset of skip(l2) for l1 < l2
+        prev = cur
+    assert prev.any()                           # lambda close to 1 does skip something
+
+
+# ---- C-P7: the error bound implied by the pruning condition ------------------
+
+@pytest.mark.parametrize("lam", [1e-3, 0.05, 0.3])
+def test_dynamic_error_within_page_bound(lam):
+    """Skipped entries satisfy S - M < ln(lambda) with M the row's global max,
+    so their weights e^{S-M} are each below lambda.  With eps the exact sum of
+    skipped weights and Z >= 1 the dense denominator,
+    |O_dyn - O_dense| <= 2 eps max|V| / Z per row and component."""
+    cfg, (q, k, v) = _concentrated_case()
+    n = cfg.N
+    vv = A.as_f64(v[0, :, 0])
+    for t in (4, 12, 15):
+        rows, out, blocks, skip, _ = A.prefill_tile(q, k, v, 0, 2, t, Br=64, Bc=32, scale=cfg.scale,
+                                                    causal=True, lam=lam, n_valid=n)
+        qr = A.as_f64(q[0, rows[0]:rows[-1] + 1, 2])
+        keys = np.arange(n)
+        allowed = keys[None, :] <= rows[:, None]
+        dense = A.masked_attention(qr, A.as_f64(k[0, :, 0]), vv, allowed, cfg.scale)
+        S = np.where(allowed, cfg.scale * qr @ A.as_f64(k[0, :, 0]).T, -np.inf)
+        Mx = S.max(1)
+        W = np.exp(S - Mx[:, None])
+        skipped_keys = np.zeros(n, bool)
+        for j in blocks[skip]:
+            skipped_keys[j * 32:(j + 1) * 32] = True
+        eps = (W * skipped_keys[None, :]).sum(1)
+        Z = W.sum(1)
+        assert np.all(W[:, skipped_keys] < lam + 1e-15)
+        bound = 2 * eps * np.abs(vv).max() / Z
+        err = np.abs(out - dense).max(1)
+        assert np.all(err <= bound + 1e-12)
+
+
+# ---- C-P8: decode equals prefill at one query row -----------------------------
+
+def test_decode_equals_prefill_single_row():
+    cfg = DecodeWorkload(name="t", description="", B=1, Hq=4, Hkv=4, L=700, d=32, Bc=64, lam=0.02, seed=9)
+    q, k, v = gen_decode_sequence(cfg, 0, L=cfg.L)
+    for g in range(4):
+        od, sd, _ = A.decode_group(q[g:g + 1], k[:, g], v[:, g], 64, cfg.scale, cfg.lam, "loop")
+        rows = np.array([cfg.L - 1])
+        op, sp, _ = A.blasst_tile(A.as_f64(q[g:g + 1]), k[:, g], v[:, g], rows, np.arange(11), 64,
+                                  cfg.scale, cfg.lam, cfg.L, True)
+        assert np.array_equal(sd, sp)
+        assert np.max(np.abs(od - op)) < 1e-12
+
+
+def test_decode_loop_equals_closed_form():
+    cfg = DecodeWorkload(name="t", description="", B=1, Hq=8, Hkv=2, L=2000, d=64, Bc=64, lam=40 / 2000, seed=11)
+    q, k, v = gen_decode_sequence(cfg, 0)
+    o1, s1, m1 = A.decode_sequence(q, k, v, 64, cfg.scale, cfg.lam, "loop")
+    o2, s2, m2 = A.decode_sequence(q, k, v, 64, cfg.scale, cfg.lam, "closed_form")
+    assert np.array_equal(s1, s2)
+    assert s1.any()
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(m1 - m2)) < 1e-9
+
+
+# ---- C-P9: merging split partials reproduces the unsplit result ---------------
+
+def test_split_merge_identity():
+    L, d = 1000, 16
+    q, k, v = _rand((3, d), 30, 2.0), _rand((L, d), 31, 2.0), _rand((L, d), 32)
+    kept = _rand((L,), 33) > -0.8
+    full = A.masked_attention(q, k, v, np.broadcast_to(kept, (3, L)), 0.3)
+    for cuts in ([0, 1000], [0, 10, 1000], [0, 128, 256, 640, 999, 1000], list(range(0, 1001, 64)) + [1000]):
+        cuts = sorted(set(cuts))
+        parts = [A.partial_state(q, k[a:b], v[a:b], np.broadcast_to(kept[a:b], (3, b - a)), 0.3)
+                 for a, b in zip(cuts[:-1], cuts[1:])]
+        merged = A.merge_partials([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
+        assert np.max(np.abs(merged - full)) < 1e-12
+
+
+def test_lambda_range_rejected():
+    for bad in (-0.1, 1.0, 2.0):
+        with pytest.raises(ValueError):
+            A.log_threshold(bad)
