@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of block-sparse / BLASST attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--no-also] [--no-cpu-baseline]
+
+One step = one pass of the attention hot path over one batch of the named
+synthetic workload, inputs resident in HBM: the prefill kernel for a prefill
+workload (the static block index is built once, on the host, before timing:
+a fixed mask is not rebuilt per step), or the decode split kernel plus its
+combine kernel for the decode workload.
+
+Prints ONE JSON line.  ``value`` is the dense-equivalent attention TFLOP/s of
+the primary workload (the multimodal DiT image+text configuration by
+default); ``also`` carries the same measurement for the other full-size
+workloads (video DiT static mask, BLASST causal prefill, BLASST decode in
+HBM GB/s), each with its roofline and its share of skipped blocks.
+
+Definitions:
+* dense-equivalent FLOPs = 4 B Hq d x (allowed query-key pairs of the full
+  problem): Nq * n_valid non-causal, N (N + 1) / 2 causal;
+* processed FLOPs (MFMA roofline numerator) = 2 Br Bc d per visited block
+  (Q K^T) + 2 Br Bc d per computed block (P V), whole blocks;
+* decode algorithmic bytes = K of every visited block + V of every computed
+  block + q + out (workspace traffic excluded);
+* % skipped = skipped / visited blocks (dynamic) or 1 - kept / all tile-blocks
+  (static).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv attention TFLOP/s (prefill), HBM GB/s (decode), % blocks skipped"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": "block_sparse_attention_flash_amd/csrc/prefill_bf16.hip",
+    "decode_split_kernel": "block_sparse_attention_flash_amd/csrc/decode.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when absent or taken on a different kernel source."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = data.get(kernel, {}).get(workload)
+    if not e or e.get("source_sha") != source_sha(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """HIP-event timing on the current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {"avg_ms": sum(per) / len(per), "median_ms": per[len(per) // 2], "min_ms": per[0], "wall_ms": wall}
+
+
+# ---------------------------------------------------------------------------- prefill
+
+def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool = False):
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_prefill_inputs
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"{name}: generating inputs ({cfg.description})")
+    q, k, v = gen_prefill_inputs(cfg, device=dev)
+    Tr, Tc = -(-cfg.N // cfg.Br), -(-cfg.N // cfg.Bc)
+    rp = ci = order = None
+    build_ms = None
+    if cfg.mask is not None:
+        t0 = time.perf_counter()
+        rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
+        order_h = bsa.tile_order_lpt(rp_h)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        rp, ci, order = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, order_h))
+    out = torch.empty_like(q)
+    counters = torch.zeros((cfg.B, cfg.Hq, Tr, 2), dtype=torch.int32, device=dev)
+
+    def call(cnt=None):
+        bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam, causal=cfg.causal, Br=cfg.Br, Bc=cfg.Bc,
+                        row_ptr=rp, col_idx=ci, tile_order=order, n_valid=cfg.n_valid, out=out, tile_counters=cnt)
+
+    call(counters)                       # untimed: counts visited / skipped blocks
+    torch.cuda.synchronize()
+    c = counters.view(-1, 2).sum(0).tolist()
+    visited, skipped = int(c[0]), int(c[1])
+    log(f"{name}: timing {steps} steps")
+    t = time_launches(call, steps, warmup)
+    per_block = 2 * cfg.Br * cfg.Bc * cfg.d
+    processed = per_block * (visited + (visited - skipped))
+    if cfg.causal:
+        pairs = cfg.N * (cfg.N + 1) // 2
+    else:
+        pairs = cfg.N * cfg.n_valid
+    dense = 4 * cfg.B * cfg.Hq * cfg.d * pairs
+    ms = t["avg_ms"]
+    achieved = processed / (ms * 1e-3) / 1e12
+    if cfg.lam > 0:
+        pct = 100.0 * skipped / max(1, visited)
+    else:
+        pct = 100.0 * (1.0 - visited / (cfg.B * cfg.Hq * Tr * Tc))
+    res = {
+        "workload": name, "description": cfg.description,
+        "value": dense / (ms * 1e-3) / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+        "ms_per_step": ms, "timing": t,
+        "processed_tflops": achieved,
+        "pct_blocks_skipped": pct,
+        "blocks": {"visited": visited, "skipped": skipped, "computed": visited - skipped,
+                   "tile_blocks_total": cfg.B * cfg.Hq * Tr * Tc},
+        "lambda": cfg.lam, "block_index_build_ms": build_ms,
+        "config": {"workload": f"{name}: {cfg.description}", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
+                   "Br": cfg.Br, "Bc": cfg.Bc, "causal": cfg.causal, "lambda": cfg.lam, "dtype": cfg.dtype},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "per_launch_flops": processed,
+                     "traffic": traffic_for("prefill_bf16_kernel", name)},
+    }
+    if keep_inputs:
+        res["_inputs"] = (cfg, q, k, v, rp, ci)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------- decode
+
+def run_decode_workload(name: str, steps: int, warmup: int):
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_decode_inputs
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"{name}: generating inputs ({cfg.description})")
+    q, kc, vc = gen_decode_inputs(cfg, device=dev)
+    Tc = -(-cfg.L // cfg.Bc)
+    ws = torch.empty(bsa.decode_workspace_size(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.Bc), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.bfloat16, device=dev)
+    counters = torch.zeros((cfg.B, cfg.Hkv, 2), dtype=torch.int32, device=dev)
+
+    def call(cnt=None):
+        bsa.decode_fwd(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=cfg.lam, Bc=cfg.Bc, workspace=ws, out=out,
+                       counters=cnt)
+
+    call(counters)
+    torch.cuda.synchronize()
+    health = bsa.decode_check(ws)
+    c = counters.view(-1, 2).sum(0).tolist()
+    visited, skipped = int(c[0]), int(c[1])
+    log(f"{name}: timing {steps} steps")
+    t = time_launches(call, steps, warmup)
+    blk_bytes = cfg.Bc * cfg.d * 2
+    algo = visited * blk_bytes + (visited - skipped) * blk_bytes + 2 * cfg.B * cfg.Hq * cfg.d * 2
+    ms = t["avg_ms"]
+    gbs = algo / (ms * 1e-3) / 1e9
+    res = {
+        "workload": name, "description": cfg.description,
+        "value": gbs, "unit": "GB/s (algorithmic HBM bytes)",
+        "ms_per_step": ms, "timing": t,
+        "pct_blocks_skipped": 100.0 * skipped / max(1, visited),
+        "blocks": {"visited": visited, "skipped": skipped, "computed": visited - skipped},
+        "lambda": cfg.lam, "num_splits": bsa.decode_num_splits(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.Bc),
+        "health": health,
+        "config": {"workload": f"{name}: {cfg.description}", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "L": cfg.L, "d": cfg.d,
+                   "Bc": cfg.Bc, "lambda": cfg.lam, "dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (+ reset and combine in the timed call)",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "per_launch_bytes": algo,
+                     "traffic": traffic_for("decode_split_kernel", name)},
+    }
+    del q, kc, vc, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------- oracle on host cores
+
+def cpu_baseline_prefill(res, budget_s: float):
+    """Time the float64 oracle (as it stands) on a bounded sample of the same
+    workload's (batch, head, tile) items and extrapolate by processed blocks."""
+    import numpy as np
+    from oracle import attention as A
+    cfg, q, k, v, rp, ci = res["_inputs"]
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    rp_h = rp.cpu().numpy() if rp is not None else None
+    ci_h = ci.cpu().numpy() if ci is not None else None
+    Tr = -(-cfg.N // cfg.Br)
+    rng = np.random.default_rng(0)
+    items = [(b, h, t) for b in range(cfg.B) for h in range(cfg.Hq) for t in range(Tr)]
+    rng.shuffle(items)
+    method = "two_pass" if cfg.lam == 0.0 else "loop"
+    done_blocks = 0
+    n_items = 0
+    t0 = time.perf_counter()
+    for (b, h, t) in items:
+        _, _, blocks, _, _ = A.prefill_tile(qh, kh, vh, b, h, t, Br=cfg.Br, Bc=cfg.Bc, scale=cfg.scale,
+                                            causal=cfg.causal, lam=cfg.lam, n_valid=cfg.n_valid,
+                                            row_ptr=rp_h, col_idx=ci_h, method=method)
+        done_blocks += len(blocks)
+        n_items += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    est = el * res["blocks"]["visited"] / max(1, done_blocks)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"), default=1)
+    except Exception:
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    dense = res["value"] * res["ms_per_step"] * 1e-3 * 1e12
+    return {"value": dense / est / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": blas or cores,
+            "host_cores_available": cores, "kind": "oracle",
+            "sample": f"{n_items} of {len(items)} (batch, head, tile) items of {res['workload']} in "
+                      f"{el:.1f} s, {done_blocks} of {res['blocks']['visited']} visited blocks; full-workload "
+                      f"time extrapolated by visited blocks to {est:.1f} s",
+            "method": f"oracle.attention.prefill_tile(method={method!r}), float64 numpy"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
+    ap.add_argument("--also", default="cfg3,cfg4,cfg5", help="comma list of further workloads ('' for none)")
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the kernels need no collectives; "
+                                   "see DESIGN.md for how the path would shard across GPUs", "n_gpus": a.gpus}))
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    import block_sparse_attention_flash_amd as bsa
+    bsa.library()
+
+    def run(name, keep=False):
+        if name == "cfg5":
+            return run_decode_workload(name, a.steps, a.warmup)
+        return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep)
+
+    torch.cuda.synchronize()
+    prim = run(a.workload, keep=not a.no_cpu_baseline)
+    cpu = None
+    if not a.no_cpu_baseline and "_inputs" in prim:
+        log(f"oracle baseline on host cores (~{a.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline_prefill(prim, a.cpu_seconds)
+    prim.pop("_inputs", None)
+    torch.cuda.empty_cache()
+    also = []
+    if not a.no_also and a.also:
+        for name in [x for x in a.also.split(",") if x and x != a.workload]:
+            r = run(name)
+            r.pop("_inputs", None)
+            also.append(r)
+    line = {
+        "metric": METRIC, "value": prim["value"], "unit": prim["unit"].split(" ")[0],
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": prim["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators shaped like the pages' workloads)",
+        "config": prim["config"],
+        "pct_blocks_skipped": prim["pct_blocks_skipped"],
+        "roofline": prim["roofline"], "cpu_baseline": cpu,
+        "primary": {k: v for k, v in prim.items() if k not in ("config", "roofline")},
+        "also": also,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,234 @@
+"""Block-sparse and BLASST flash attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbsattn.so`` (``include/bsattn.h``).
+It only marshals arguments: torch tensors supply device pointers, strides and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels (or, for the block index, its host C++ builder).  If the library
+is missing the binding raises; there is no fallback implementation.
+
+Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
+
+* ``build_block_index(spec, n_q, n_k, Br, Bc)`` -> (row_ptr, col_idx) int32 numpy
+* ``validate_block_index(row_ptr, col_idx, Tc)``
+* ``tile_order_lpt(row_ptr)`` -> int32 numpy launch order
+* ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
+* ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
+* ``decode_workspace_size(...)``, ``decode_num_splits(...)``, ``decode_check(workspace)``
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import _abi
+
+__all__ = [
+    "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
+    "prefill_fwd", "decode_fwd", "decode_workspace_size", "decode_num_splits", "decode_check",
+]
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_LIB: Optional[C.CDLL] = None
+
+
+def library() -> C.CDLL:
+    """The loaded libbsattn (raises if it has not been built).
+
+    The library shares the HIP runtime of the host process.  Its code objects
+    register with that runtime when it is loaded, so torch's HIP context is
+    brought up first when a GPU is present (loading it before the runtime has
+    enumerated devices leaves the library's launches without a device)."""
+    global _LIB
+    if _LIB is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                torch.cuda.init()
+        except ImportError:  # pragma: no cover - C-only callers manage HIP themselves
+            pass
+        _LIB = _abi.load()
+    return _LIB
+
+
+def _status_name(st: int) -> str:
+    try:
+        return library().bsattn_status_string(st).decode()
+    except Exception:  # pragma: no cover
+        return f"status {st}"
+
+
+def _check(st: int):
+    if st != _abi.BSATTN_OK:
+        raise BsattnError(st, library().bsattn_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# block index (host)
+# ---------------------------------------------------------------------------
+
+def _c_spec(spec):
+    segs = list(spec.segments)
+    arr = (_abi.Segment * max(1, len(segs)))()
+    for i, s in enumerate(segs):
+        arr[i] = _abi.Segment(int(s.kind), int(s.start), int(getattr(s, "length", getattr(s, "len", 0))),
+                              int(s.frames), int(s.grid_h), int(s.grid_w), int(s.radius), int(s.t_radius),
+                              int(s.unit))
+    cs = _abi.MaskSpec(int(spec.n_valid), len(segs), C.cast(arr, C.POINTER(_abi.Segment)),
+                       int(spec.anchor_start), int(spec.anchor_len))
+    return cs, arr
+
+
+def build_block_index(spec, n_q: int, n_k: int, Br: int, Bc: int):
+    """Per-query-tile CSR of kept key blocks for a mask specification.
+
+    ``spec`` is any object with ``n_valid``, ``segments`` (objects with kind,
+    start, length, frames, grid_h, grid_w, radius, t_radius, unit),
+    ``anchor_start`` and ``anchor_len``."""
+    lib = library()
+    cs, keep = _c_spec(spec)
+    Tr = -(-n_q // Br)
+    row_ptr = np.zeros(Tr + 1, dtype=np.int32)
+    nnz = C.c_int64(0)
+    _check(lib.bsattn_build_block_index(C.byref(cs), n_q, n_k, Br, Bc, row_ptr.ctypes.data, None, 0, C.byref(nnz)))
+    col_idx = np.zeros(max(1, nnz.value), dtype=np.int32)
+    _check(lib.bsattn_build_block_index(C.byref(cs), n_q, n_k, Br, Bc, row_ptr.ctypes.data, col_idx.ctypes.data,
+                                        col_idx.size, C.byref(nnz)))
+    del keep
+    return row_ptr, col_idx[:nnz.value].copy()
+
+
+def validate_block_index(row_ptr, col_idx, Tc: int):
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    _check(library().bsattn_validate_block_index(row_ptr.ctypes.data, col_idx.ctypes.data if col_idx.size else None,
+                                                 row_ptr.size - 1, Tc))
+
+
+def tile_order_lpt(row_ptr):
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    order = np.zeros(row_ptr.size - 1, dtype=np.int32)
+    _check(library().bsattn_tile_order_lpt(row_ptr.ctypes.data, row_ptr.size - 1, order.ctypes.data))
+    return order
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
+                Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
+                out=None, tile_counters=None, block_state=None, stream=None):
+    """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
+
+    ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
+    ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
+    [B, Hq, Tr, Tc] are optional device outputs.  Returns ``out``."""
+    torch = _torch()
+    if q.dtype == torch.bfloat16:
+        dt = _abi.BSATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = _abi.BSATTN_FP32
+    else:
+        raise BsattnError(_abi.BSATTN_ERR_UNSUPPORTED, f"dtype {q.dtype} not supported")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, f"{name} must be [B, N, H, d] with d contiguous")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _abi.PrefillArgs()
+    a.dtype = dt
+    a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
+    a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d = B, Hq, Hkv, Nq, Nk, d
+    for fld, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, fld)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    a.row_ptr, a.col_idx, a.tile_order = _ptr(row_ptr), _ptr(col_idx), _ptr(tile_order)
+    a.n_valid = int(n_valid)
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.lam = float(lam)
+    a.causal = 1 if causal else 0
+    a.Br, a.Bc = int(Br), int(Bc)
+    a.tile_counters, a.block_state = _ptr(tile_counters), _ptr(block_state)
+    _check(library().bsattn_prefill_fwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
+    return out
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:
+    return int(library().bsattn_decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits))
+
+
+def decode_num_splits(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:
+    return int(library().bsattn_decode_num_splits(B, Hq, Hkv, L, d, Bc, num_splits))
+
+
+def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
+               Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
+               stream=None):
+    """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``decode_workspace_size`` bytes (allocated here if None)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    L = Lmax if L is None else int(L)
+    if k_cache.stride() != v_cache.stride():
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "k_cache and v_cache must share strides")
+    if q.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "head dim must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    need = decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _abi.DecodeArgs()
+    a.q, a.k_cache, a.v_cache, a.out = _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out)
+    a.B, a.Hq, a.Hkv, a.L, a.Lmax, a.d = B, Hq, Hkv, L, Lmax, d
+    a.q_stride[:] = [q.stride(0), q.stride(1)]
+    a.kv_stride[:] = [k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)]
+    a.o_stride[:] = [out.stride(0), out.stride(1)]
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.lam = float(lam)
+    a.Bc = int(Bc)
+    a.num_splits = int(num_splits)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    a.counters, a.block_state = _ptr(counters), _ptr(block_state)
+    _check(library().bsattn_decode_fwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
+    return out
+
+
+def decode_check(workspace) -> int:
+    """Health word of the last decode on this workspace (synchronous read): 0 = fine."""
+    h = C.c_int32(0)
+    _check(library().bsattn_decode_check(C.c_void_p(_ptr(workspace)), C.byref(h)))
+    return int(h.value)

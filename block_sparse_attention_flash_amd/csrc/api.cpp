@@ -1,0 +1,229 @@
+// C-ABI entry points of libbsattn: argument validation, error reporting and
+// dispatch to the HIP kernels.  Nothing here allocates device memory or
+// synchronises a stream (bsattn_decode_check aside, which is a documented
+// synchronous read of one workspace word).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace bsattn {
+
+static thread_local char g_err[512] = {0};
+
+bsattn_status fail(bsattn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bsattn_status check_strides(const char* name, const int64_t* s, int n, int64_t vec) {
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(BSATTN_ERR_INVALID_ARG, "%s stride %d is negative", name, i);
+    if (s[i] % vec != 0)
+      return fail(BSATTN_ERR_UNSUPPORTED, "%s stride %d (%lld) must be a multiple of %lld elements", name, i,
+                  (long long)s[i], (long long)vec);
+  }
+  return BSATTN_OK;
+}
+
+static bsattn_status hip_status(int e, const char* what) {
+  if (e == 0) return BSATTN_OK;
+  return fail(BSATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(e)));
+}
+
+// ---------------------------------------------------------------------------
+// decode split policy and workspace layout
+// ---------------------------------------------------------------------------
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+DecodeWorkspace decode_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t S) {
+  DecodeWorkspace w{};
+  const size_t units = (size_t)B * Hkv * S;
+  const int32_t G = Hq / Hkv;
+  size_t off = 0;
+  w.header = off; off = align256(off + 16 * sizeof(int32_t));
+  w.flags = off;  off = align256(off + units * sizeof(int32_t));
+  w.agg = off;    off = align256(off + units * 16 * sizeof(float));
+  w.incl = off;   off = align256(off + units * 16 * sizeof(float));
+  w.stats = off;  off = align256(off + units * G * 2 * sizeof(float));
+  w.acc = off;    off = align256(off + units * G * (size_t)d * sizeof(float));
+  w.counts = off; off = align256(off + units * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+// Largest split (in Bc-blocks) whose scores fit the kernel's LDS score buffer
+// (8192 floats) for G query heads.
+static int32_t max_blocks_per_split(int32_t G) {
+  int32_t m = 8192 / (64 * G);
+  return m > 64 ? 64 : m;
+}
+
+int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int32_t requested,
+                             int32_t* blocks_per_split) {
+  const int32_t cap = max_blocks_per_split(G);
+  int32_t bps;
+  if (requested > 0) {
+    int32_t S = requested < Tc ? requested : Tc;
+    bps = (Tc + S - 1) / S;
+  } else {
+    // aim for at least ~2048 split work-groups (8 per CU on 256 CUs), splits of 2..cap blocks
+    int64_t want = ((int64_t)Tc * B * Hkv + 2047) / 2048;
+    bps = (int32_t)(want < 2 ? 2 : (want > 32 ? 32 : want));
+  }
+  if (bps > cap) bps = cap;
+  if (bps < 1) bps = 1;
+  *blocks_per_split = bps;
+  return (Tc + bps - 1) / bps;
+}
+
+}  // namespace bsattn
+
+using namespace bsattn;
+
+extern "C" {
+
+const char* bsattn_status_string(int status) {
+  switch (status) {
+    case BSATTN_OK: return "BSATTN_OK";
+    case BSATTN_ERR_INVALID_ARG: return "BSATTN_ERR_INVALID_ARG";
+    case BSATTN_ERR_UNSUPPORTED: return "BSATTN_ERR_UNSUPPORTED";
+    case BSATTN_ERR_CAPACITY: return "BSATTN_ERR_CAPACITY";
+    case BSATTN_ERR_HIP: return "BSATTN_ERR_HIP";
+    default: return "BSATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* bsattn_last_error(void) { return g_err; }
+
+int bsattn_version(void) { return 0x000100; }
+
+bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSATTN_BF16 && a->dtype != BSATTN_FP32)
+    return fail(BSATTN_ERR_UNSUPPORTED, "dtype %d not supported", a->dtype);
+  if (!a->q || !a->k || !a->v || !a->out) return fail(BSATTN_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+    return fail(BSATTN_ERR_UNSUPPORTED, "q, k, v, out must be 16-byte aligned");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Nq < 1 || a->Nk < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "B, Hq, Hkv, Nq, Nk must be >= 1");
+  if (a->Hq % a->Hkv != 0) return fail(BSATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", a->d);
+  const int64_t vec = a->dtype == BSATTN_BF16 ? 8 : 4;
+  bsattn_status st;
+  if ((st = check_strides("q", a->q_stride, 3, vec)) != BSATTN_OK) return st;
+  if ((st = check_strides("k", a->k_stride, 3, vec)) != BSATTN_OK) return st;
+  if ((st = check_strides("v", a->v_stride, 3, vec)) != BSATTN_OK) return st;
+  if ((st = check_strides("out", a->o_stride, 3, vec)) != BSATTN_OK) return st;
+  if ((a->row_ptr == nullptr) != (a->col_idx == nullptr))
+    return fail(BSATTN_ERR_INVALID_ARG, "row_ptr and col_idx must both be set or both be NULL");
+  if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return fail(BSATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!(a->lambda >= 0.0f && a->lambda < 1.0f)) return fail(BSATTN_ERR_INVALID_ARG, "lambda must lie in [0, 1)");
+  if (a->causal && a->Nq != a->Nk) return fail(BSATTN_ERR_INVALID_ARG, "causal attention requires Nq == Nk");
+  if (a->n_valid < 0 || a->n_valid > a->Nk) return fail(BSATTN_ERR_INVALID_ARG, "n_valid must lie in [0, Nk]");
+  if (a->Bc != 64) return fail(BSATTN_ERR_UNSUPPORTED, "Bc must be 64");
+  if (a->dtype == BSATTN_BF16 && a->Br != 128) return fail(BSATTN_ERR_UNSUPPORTED, "bf16 path needs Br = 128");
+  if (a->dtype == BSATTN_FP32 && a->Br != 64 && a->Br != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fp32 path needs Br in {64, 128}");
+  PrefillParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Nk = a->Nk; p.d = a->d;
+  p.qs_b = a->q_stride[0]; p.qs_t = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.ks_b = a->k_stride[0]; p.ks_t = a->k_stride[1]; p.ks_h = a->k_stride[2];
+  p.vs_b = a->v_stride[0]; p.vs_t = a->v_stride[1]; p.vs_h = a->v_stride[2];
+  p.os_b = a->o_stride[0]; p.os_t = a->o_stride[1]; p.os_h = a->o_stride[2];
+  p.row_ptr = a->row_ptr; p.col_idx = a->col_idx; p.tile_order = a->tile_order;
+  p.n_valid = a->n_valid == 0 ? a->Nk : a->n_valid;
+  p.scale = a->scale; p.lambda = a->lambda; p.causal = a->causal ? 1 : 0;
+  p.Br = a->Br; p.Bc = a->Bc;
+  p.Tr = (a->Nq + a->Br - 1) / a->Br;
+  p.Tc = (a->Nk + a->Bc - 1) / a->Bc;
+  p.tile_counters = a->tile_counters; p.block_state = a->block_state;
+  if ((int64_t)p.B * p.Hq * p.Tr > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  int e = a->dtype == BSATTN_BF16 ? launch_prefill_bf16(p, stream) : launch_prefill_f32(p, stream);
+  return hip_status(e, "prefill launch");
+}
+
+size_t bsattn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d, int32_t Bc,
+                                    int32_t num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || Bc < 1 || Hq % Hkv) return 0;
+  int32_t bps;
+  int32_t Tc = (L + Bc - 1) / Bc;
+  int32_t S = decode_choose_splits(B, Hkv, Tc, Hq / Hkv, num_splits, &bps);
+  return decode_workspace_layout(B, Hq, Hkv, d, S).total;
+}
+
+int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d, int32_t Bc,
+                                 int32_t num_splits) {
+  (void)d;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || Bc < 1 || Hq % Hkv) return 0;
+  int32_t bps;
+  return decode_choose_splits(B, Hkv, (L + Bc - 1) / Bc, Hq / Hkv, num_splits, &bps);
+}
+
+bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
+  if (!a->q || !a->k_cache || !a->v_cache || !a->out || !a->workspace)
+    return fail(BSATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, out, workspace must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->out))
+    return fail(BSATTN_ERR_UNSUPPORTED, "q, k_cache, v_cache, out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->L < 1 || a->Lmax < a->L)
+    return fail(BSATTN_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and 1 <= L <= Lmax");
+  if (a->Hq % a->Hkv != 0) return fail(BSATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  const int32_t G = a->Hq / a->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(BSATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d not supported (1, 2, 4, 8)", G);
+  if (a->d != 64 && a->d != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", a->d);
+  if (a->Bc != 64) return fail(BSATTN_ERR_UNSUPPORTED, "Bc must be 64");
+  if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return fail(BSATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!(a->lambda >= 0.0f && a->lambda < 1.0f)) return fail(BSATTN_ERR_INVALID_ARG, "lambda must lie in [0, 1)");
+  if (a->num_splits < 0) return fail(BSATTN_ERR_INVALID_ARG, "num_splits must be >= 0");
+  bsattn_status st;
+  if ((st = check_strides("q", a->q_stride, 2, 8)) != BSATTN_OK) return st;
+  if ((st = check_strides("kv", a->kv_stride, 3, 8)) != BSATTN_OK) return st;
+  if ((st = check_strides("out", a->o_stride, 2, 8)) != BSATTN_OK) return st;
+  DecodeParams p{};
+  p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.out = a->out;
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.L = a->L; p.d = a->d; p.G = G;
+  p.qs_b = a->q_stride[0]; p.qs_h = a->q_stride[1];
+  p.ks_b = a->kv_stride[0]; p.ks_t = a->kv_stride[1]; p.ks_h = a->kv_stride[2];
+  p.os_b = a->o_stride[0]; p.os_h = a->o_stride[1];
+  p.scale = a->scale; p.lambda = a->lambda; p.Bc = a->Bc;
+  p.Tc = (a->L + a->Bc - 1) / a->Bc;
+  p.num_splits = decode_choose_splits(a->B, a->Hkv, p.Tc, G, a->num_splits, &p.blocks_per_split);
+  const DecodeWorkspace w = decode_workspace_layout(a->B, a->Hq, a->Hkv, a->d, p.num_splits);
+  if (a->workspace_bytes < w.total)
+    return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
+  if ((int64_t)a->B * a->Hkv * p.num_splits > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  p.workspace = a->workspace; p.counters = a->counters; p.block_state = a->block_state;
+  return hip_status(launch_decode(p, stream), "decode launch");
+}
+
+bsattn_status bsattn_decode_check(const void* workspace, int32_t* health_out) {
+  clear_error();
+  if (!workspace || !health_out) return fail(BSATTN_ERR_INVALID_ARG, "workspace and health_out must be non-NULL");
+  int32_t h = 0;
+  hipError_t e = hipMemcpy(&h, static_cast<const char*>(workspace) + sizeof(int32_t), sizeof(int32_t),
+                           hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  *health_out = h;
+  return BSATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Device helpers for the gfx950 (CDNA4) kernels of libbsattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace bsattn {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// v_exp_f32: 2^x (flushes results below the float range to 0; 2^-inf = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 32x32x16 bf16 MFMA.  Lane l holds A[m = l%32][k = 8*(l/32) + i] and
+// B[k = 8*(l/32) + i][n = l%32], i = 0..7; accumulator element a of lane l is
+// D[m = 8*(a/4) + 4*(l/32) + a%4][n = l%32].  (Checked on the device.)
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 MFMA.  Lane l holds A[m = l%16][k = 8*(l/16) + i] and
+// B[k = 8*(l/16) + i][n = l%16]; accumulator element a of lane l is
+// D[m = 4*(l/16) + a][n = l%16].  (Checked on the device.)
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16 on an LDS address.  Within each group of 16 lanes, lane
+// j receives, in slot s (0..3), the 16-bit element j%4 of the 8 bytes
+// addressed by lane 4*s + j/4 of the same group.  (Checked on the device.)
+__device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x4(i16x4 lo, i16x4 hi) {
+  union {
+    i16x4 h[2];
+    bf16x8 v;
+  } u;
+  u.h[0] = lo;
+  u.h[1] = hi;
+  return u.v;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+  f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+}  // namespace bsattn

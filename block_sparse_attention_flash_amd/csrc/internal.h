@@ -1,0 +1,83 @@
+// Internal declarations shared by the host-side translation units of libbsattn.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/bsattn.h"
+
+namespace bsattn {
+
+// thread-local error message (api.cpp)
+bsattn_status fail(bsattn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+bsattn_status validate_spec(const bsattn_mask_spec* spec, int32_t n_k);
+bsattn_status build_block_index(const bsattn_mask_spec* spec, int32_t n_q, int32_t n_k, int32_t Br, int32_t Bc,
+                                std::vector<int32_t>& row_ptr, std::vector<int32_t>& col_idx);
+
+// Validated, normalised launch parameters.  Strides are in elements.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* tile_order;
+  int32_t n_valid;
+  float scale;
+  float lambda;
+  int32_t causal;
+  int32_t Br, Bc;
+  int32_t Tr, Tc;
+  int32_t* tile_counters;
+  uint8_t* block_state;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int32_t B, Hq, Hkv, L, d, G;
+  int64_t qs_b, qs_h;
+  int64_t ks_b, ks_t, ks_h;  // shared by k and v
+  int64_t os_b, os_h;
+  float scale;
+  float lambda;
+  int32_t Bc;
+  int32_t Tc;
+  int32_t num_splits;      // per (sequence, kv head)
+  int32_t blocks_per_split;
+  void* workspace;
+  int32_t* counters;
+  uint8_t* block_state;
+};
+
+// Decode workspace layout (all offsets 256-byte aligned), see decode.hip.
+struct DecodeWorkspace {
+  size_t header;    // [0]: ticket counter, [1]: health word
+  size_t flags;     // int32 [B*Hkv*S]
+  size_t agg;       // float [B*Hkv*S*16]  split aggregate max per row
+  size_t incl;      // float [B*Hkv*S*16]  inclusive prefix max per row
+  size_t stats;     // float [B*Hkv*S*G*2] partial (m, l)
+  size_t acc;       // float [B*Hkv*S*G*d] partial unnormalised output
+  size_t counts;    // int32 [B*Hkv*S] skipped blocks per split
+  size_t total;
+};
+DecodeWorkspace decode_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t S);
+int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int32_t requested,
+                             int32_t* blocks_per_split);
+
+// Kernel launchers (HIP translation units).  Return hipError_t as int.
+int launch_prefill_bf16(const PrefillParams& p, void* stream);
+int launch_prefill_f32(const PrefillParams& p, void* stream);
+int launch_decode(const DecodeParams& p, void* stream);
+
+}  // namespace bsattn

@@ -1,0 +1,326 @@
+// bf16 prefill on CDNA4 matrix cores: block-sparse / BLASST flash attention.
+//
+// One work-group (4 waves, 256 threads) owns a tile of Br = 128 query rows
+// of one (batch, query head); wave w owns rows 32w..32w+31.  The tile walks
+// its visited key blocks (Bc = 64) in ascending order: the CSR list of a
+// static block mask (DiT article section 3.3: the list is consulted before
+// any K/V load) or every block up to the diagonal.  Per block:
+//
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS, Q held in registers
+//   block row max, running max (BLASST notes Algorithm 1, lines 5-6)
+//   [lambda > 0] tile-wide vote: block max - running max < ln(lambda) in
+//                every row (notes section 3.1.1; per-lane predicate, wave
+//                ballot, one LDS word per wave, as in notes section 4)
+//   if kept:     P = 2^(S*scale*log2e - m),  l += rowsum(P),
+//                O^T += V^T P^T  (V read transposed from LDS with
+//                ds_read_b64_tr_b16)
+//
+// Layout choice: computing S^T (keys x rows) puts one query row per lane
+// (row = lane % 32, split over lanes l and l+32), so the row max, the row
+// sum and the rescale factor are per-lane values, and the S^T accumulator
+// is already the B operand of the O^T MFMA after a bf16 pack - no LDS
+// round trip for P.  O^T keeps the row in the lane as well, so rescaling O
+// is a per-lane multiply.
+//
+// The running max is rescaled lazily: the reference max used in the
+// exponent moves only when a row's max grows by more than 2^8, which keeps
+// P <= 256 (exact in the bf16/fp32 ranges) and removes most O rescales.
+// The skip test always uses the true running max.
+//
+// K/V blocks are staged global -> registers -> LDS, double buffered, with
+// one barrier per block (two when the vote is on).  As in the BLASST notes
+// section 4.1, the prefill still streams V for blocks it skips: prefill is
+// compute bound and the load is issued one block ahead, before the skip
+// decision is known.
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int BR = 128;
+constexpr int BC = 64;
+constexpr int NT = 256;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+
+template <int D>
+struct Smem {
+  static constexpr int PITCH = D + 8;  // bf16 elements per LDS row (16 B pad against bank conflicts)
+  __bf16 k[2][BC * PITCH];
+  __bf16 v[2][BC * PITCH];
+  int vote[2][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block_regs(u32x4 (&kr)[D / 32], u32x4 (&vr)[D / 32], const __bf16* kbase,
+                                                const __bf16* vbase, int64_t ks_t, int64_t vs_t, int j, int Nk,
+                                                int tid) {
+  // D/8 chunks of 16 B per key row; 64 * D/8 chunks per block; NT threads
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / (D / 8), c8 = c % (D / 8);
+    const int key = j * BC + r;
+    if (key < Nk) {
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * ks_t + c8 * 8);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * vs_t + c8 * 8);
+    } else {
+      kr[i] = u32x4{0, 0, 0, 0};
+      vr[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_block_lds(const u32x4 (&kr)[D / 32], const u32x4 (&vr)[D / 32], __bf16* ks,
+                                                __bf16* vs, int tid) {
+  constexpr int PITCH = Smem<D>::PITCH;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / (D / 8), c8 = c % (D / 8);
+    *reinterpret_cast<u32x4*>(ks + r * PITCH + c8 * 8) = kr[i];
+    *reinterpret_cast<u32x4*>(vs + r * PITCH + c8 * 8) = vr[i];
+  }
+}
+
+template <int D, bool CAUSAL, bool DYN>
+__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams p) {
+  constexpr int PITCH = Smem<D>::PITCH;
+  constexpr int KS = D / 16;  // k-steps of the S MFMA
+  constexpr int NTD = D / 32; // 32-wide d tiles of the O MFMA
+  __shared__ Smem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- work item: XCD-aware mapping (WG i runs on XCD i % 8), then
+  //      (batch, kv head, tile rank, head in group) with heads innermost so
+  //      the G heads sharing K/V run together on one XCD.
+  const int G = p.Hq / p.Hkv;
+  const int64_t W = (int64_t)p.B * p.Hq * p.Tr;
+  int64_t wi = blockIdx.x;
+  if ((W & 7) == 0) wi = (wi & 7) * (W >> 3) + (wi >> 3);
+  const int hh = (int)(wi % G);
+  wi /= G;
+  const int rank = (int)(wi % p.Tr);
+  wi /= p.Tr;
+  const int g = (int)(wi % p.Hkv);
+  const int b = (int)(wi / p.Hkv);
+  const int h = g * G + hh;
+  const int t = p.tile_order ? p.tile_order[rank] : (CAUSAL ? p.Tr - 1 - rank : rank);
+
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
+
+  const int row = t * BR + wave * 32 + l32;  // this lane's query row
+  const bool row_ok = row < p.Nq;
+
+  // Q fragment (B operand of S^T = K Q^T): lane holds Q[row][16 ks + 8 hi + 0..7]
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row_ok)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (int64_t)row * p.qs_t + 16 * ks + 8 * hi);
+    else
+      qf[ks] = bf16x8{};
+  }
+
+  // visited blocks
+  const int last_row = min(t * BR + BR, p.Nq) - 1;
+  int beg = 0, nblk;
+  const int32_t* cols = nullptr;
+  if (p.row_ptr) {
+    beg = p.row_ptr[t];
+    const int end = p.row_ptr[t + 1];
+    cols = p.col_idx + beg;
+    nblk = end - beg;
+    if (CAUSAL) {  // ascending list: keep entries with j*BC <= last_row
+      int lo = 0, hi2 = nblk;
+      while (lo < hi2) {
+        const int mid = (lo + hi2) >> 1;
+        if (cols[mid] * BC <= last_row) lo = mid + 1; else hi2 = mid;
+      }
+      nblk = lo;
+    }
+  } else {
+    nblk = CAUSAL ? min(p.Tc, last_row / BC + 1) : p.Tc;
+  }
+
+  const float c2 = p.scale * kLog2e;                    // raw score -> log2 units
+  const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
+  float m_run = kNegInf;   // true running max (raw score units)
+  float m_ref = kNegInf;   // reference max used in the exponent (raw units)
+  float l_part = 0.0f;     // this lane's half of the row sum
+  f32x16 oacc[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
+  int skipped = 0;
+
+  u32x4 kr[D / 32], vr[D / 32];
+  if (nblk > 0) {
+    const int j0 = cols ? cols[0] : 0;
+    load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, j0, p.Nk, tid);
+    store_block_lds<D>(kr, vr, sm.k[0], sm.v[0], tid);
+  }
+
+  for (int it = 0; it < nblk; ++it) {
+    const int buf = it & 1;
+    const int j = cols ? cols[it] : it;
+    __syncthreads();  // block it in LDS; everyone is done with block it-1
+    const bool more = it + 1 < nblk;
+    if (more) {
+      const int jn = cols ? cols[it + 1] : it + 1;
+      load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, jn, p.Nk, tid);
+    }
+    const __bf16* ks = sm.k[buf];
+    const __bf16* vs = sm.v[buf];
+
+    // ---- S^T = K Q^T : two 32-key tiles
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks_ = 0; ks_ < KS; ++ks_) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + l32) * PITCH + 16 * ks_ + 8 * hi);
+        sacc[mt] = mfma32(a, qf[ks_], sacc[mt]);
+      }
+    }
+
+    // ---- masks: causal diagonal, invalid keys, rows past Nq
+    const bool need_mask = (j * BC + BC > p.n_valid) || (CAUSAL && j * BC + BC - 1 > t * BR);
+    if (need_mask || !row_ok) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = j * BC + 32 * mt + 8 * (a >> 2) + 4 * hi + (a & 3);
+          const bool ok = row_ok && key < p.n_valid && (!CAUSAL || key <= row);
+          if (!ok) sacc[mt][a] = kNegInf;
+        }
+      }
+    }
+
+    // ---- block row max and running max
+    float mb = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) mb = fmaxf(mb, sacc[mt][a]);
+    mb = wave_max_xor32(mb);
+    const float m_new = fmaxf(m_run, mb);
+
+    bool skip = false;
+    if (DYN) {
+      const bool agree = (mb == kNegInf) || ((mb - m_new) * c2 < log2_lambda);
+      const bool wave_all = __all(agree);
+      if (lane == 0) sm.vote[buf][wave] = wave_all ? 1 : 0;
+      __syncthreads();
+      skip = (sm.vote[buf][0] & sm.vote[buf][1] & sm.vote[buf][2] & sm.vote[buf][3]) != 0;
+      if (p.block_state && tid == 0)
+        p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = skip ? 2 : 1;
+    } else if (p.block_state && tid == 0) {
+      p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = 1;
+    }
+    m_run = m_new;
+
+    if (!skip) {
+      // ---- lazy rescale of the reference max
+      const bool need = (m_new != kNegInf) && (m_ref == kNegInf || (m_new - m_ref) * c2 > kTau);
+      if (__any(need)) {
+        const float alpha = need ? ((m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c2)) : 1.0f;
+        if (need) m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) oacc[n][a] *= alpha;
+      }
+      const float mref2 = (m_ref == kNegInf) ? 0.0f : m_ref * c2;
+      // ---- P = 2^(S*c2 - m_ref*c2), row sum, pack to bf16 B-operand fragments
+      bf16x8 pf[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float e = fast_exp2(fmaf(sacc[mt][8 * hf + i], c2, -mref2));
+            pv[i] = e;
+            l_part += e;
+          }
+          pf[2 * mt + hf] = to_bf16x8(pv);
+        }
+      }
+      // ---- O^T += V^T P^T : 4 key steps of 16 x NTD d tiles
+      const int g16 = lane >> 4, j16 = lane & 15;
+      const int vrow = 4 * (g16 >> 1) + (j16 >> 2);
+      const int vcol = 16 * (g16 & 1) + 4 * (j16 & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) {
+          const __bf16* src = vs + (16 * kk + vrow) * PITCH + 32 * n + vcol;
+          const i16x4 lo = lds_read_tr16(src);
+          const i16x4 hi4 = lds_read_tr16(src + 8 * PITCH);
+          oacc[n] = mfma32(join_bf16x4(lo, hi4), pf[kk], oacc[n]);
+        }
+      }
+    } else {
+      ++skipped;
+    }
+
+    if (more) store_block_lds<D>(kr, vr, sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
+  }
+
+  // ---- epilogue: O / l, bf16 store
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (row_ok) {
+    __bf16* obase = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dcol = 32 * n + 8 * q4 + 4 * hi;
+        f32x4 v4 = {oacc[n][4 * q4 + 0] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
+                    oacc[n][4 * q4 + 3] * inv};
+        *reinterpret_cast<bf16x4*>(obase + dcol) = __builtin_convertvector(v4, bf16x4);
+      }
+    }
+  }
+  if (p.tile_counters && tid == 0) {
+    int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
+    tc[0] = nblk;
+    tc[1] = skipped;
+  }
+}
+
+template <int D, bool CAUSAL, bool DYN>
+hipError_t launch(const PrefillParams& p, hipStream_t s) {
+  const int64_t grid = (int64_t)p.B * p.Hq * p.Tr;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, DYN>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_d(const PrefillParams& p, hipStream_t s) {
+  const bool dyn = p.lambda > 0.0f;
+  if (p.causal) return dyn ? launch<D, true, true>(p, s) : launch<D, true, false>(p, s);
+  return dyn ? launch<D, false, true>(p, s) : launch<D, false, false>(p, s);
+}
+
+}  // namespace
+
+int launch_prefill_bf16(const PrefillParams& p, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return p.d == 64 ? dispatch_d<64>(p, s) : dispatch_d<128>(p, s);
+}
+
+}  // namespace bsattn

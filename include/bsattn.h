@@ -1,0 +1,213 @@
+/*
+ * bsattn.h - block-sparse and BLASST attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsattn.so.  Every function has C linkage, throws nothing, and
+ * reports errors through its return status plus a thread-local message
+ * (bsattn_last_error).  The library never allocates, frees or copies device
+ * memory and never synchronises: compute entry points validate their
+ * arguments on the host, then enqueue kernels on the caller's stream and
+ * return.  All buffers are owned by the caller and must stay valid and
+ * unmodified until the enqueued work has finished.
+ *
+ * Operation (the attention operator of the BLASST paper notes, section
+ * 3.1.1):  out = softmax(scale * Q K^T) V, computed FlashAttention-style
+ * (online softmax, attention tutorial section 4.2) over tiles of Br query
+ * rows and blocks of Bc keys, where whole key blocks are skipped in two ways:
+ *
+ *   static  - a per-query-tile list of kept key blocks (CSR), built from a
+ *             mask specification (DiT block-sparse article, sections 2.1,
+ *             2.3 and 3.2; the kernel checks the list before loading K/V,
+ *             section 3.3);
+ *   dynamic - BLASST (paper notes, section 3.1 and Algorithm 1): after the
+ *             running row max is updated with a block's row max, the block
+ *             is skipped (no exponent, no row-sum update, no P.V product)
+ *             when block max - running max < ln(lambda) holds for every row
+ *             of the tile (tile-wide vote, notes section 4).  The decode
+ *             path also skips the V-block load (notes, section 4.2).
+ *
+ * Semantics fixed where the pages are open:
+ *   - scores are compared in the scaled domain (S = scale * Q K^T);
+ *   - "<" is strict; lambda = 0 disables skipping; lambda must be in [0, 1);
+ *   - key blocks are visited in ascending order (CSR order);
+ *   - a row with no allowed key in a block satisfies the skip condition;
+ *   - a query row with no allowed key at all produces zeros;
+ *   - GQA: query head h reads K/V head h / (Hq / Hkv);
+ *   - decode: the vote is taken by the G = Hq/Hkv query heads that share a
+ *     K/V head, and the running max spans the whole sequence, so the skip
+ *     set does not depend on num_splits.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* status                                                                     */
+/* ------------------------------------------------------------------------ */
+
+typedef enum {
+  BSATTN_OK = 0,
+  BSATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, lambda out of range, malformed CSR */
+  BSATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (dtype, d, tile) */
+  BSATTN_ERR_CAPACITY = 3,    /* caller buffer too small (col_idx capacity, workspace) */
+  BSATTN_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} bsattn_status;
+
+typedef enum { BSATTN_BF16 = 0, BSATTN_FP32 = 1 } bsattn_dtype;
+
+/* Static string for a status code. */
+const char* bsattn_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* bsattn_last_error(void);
+/* Library version, e.g. 0x000100 for 0.1.0. */
+int bsattn_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* mask specification and block index (host only)                             */
+/* DiT block-sparse article: section 2.1 (mask families), 2.3 (block grid,   */
+/* sparse index), 3.1 (block boundaries aligned with the token layout), 3.2  */
+/* (multimodal recipe: segments -> per-pair rule -> 0/1 block matrix).       */
+/* ------------------------------------------------------------------------ */
+
+enum {
+  BSATTN_SEG_FULL = 0,     /* every token of the segment pairs with every other (block diagonal) */
+  BSATTN_SEG_BLOCKWIN = 1, /* |(i-start)/unit - (j-start)/unit| <= radius (1-D local window)       */
+  BSATTN_SEG_IMAGE2D = 2,  /* grid_h x grid_w row-major patches: |drow| <= radius && |dcol| <= radius */
+  BSATTN_SEG_VIDEO3D = 3   /* frames x grid_h x grid_w: same frame as IMAGE2D; frames 1..t_radius
+                              apart pair iff both tokens lie in the same spatial unit
+                              ((offset within frame) / unit equal)                                  */
+};
+
+typedef struct {
+  int32_t kind;   /* BSATTN_SEG_* */
+  int32_t start;  /* first token of the segment */
+  int32_t len;    /* number of tokens (frames*grid_h*grid_w for VIDEO3D, grid_h*grid_w for IMAGE2D) */
+  int32_t frames, grid_h, grid_w;
+  int32_t radius;   /* spatial / 1-D window radius (patches, or units for BLOCKWIN) */
+  int32_t t_radius; /* temporal radius in frames (VIDEO3D) */
+  int32_t unit;     /* unit size in tokens (BLOCKWIN window unit, VIDEO3D spatial unit) */
+} bsattn_segment;
+
+typedef struct {
+  int32_t n_valid;                 /* tokens >= n_valid are padding: never keys, pair with nothing */
+  int32_t n_segments;              /* segments must not overlap */
+  const bsattn_segment* segments;  /* host memory */
+  int32_t anchor_start, anchor_len;/* global anchor tokens: pair with every valid token both ways */
+} bsattn_mask_spec;
+
+/*
+ * Build the per-query-tile CSR of kept key blocks.  Token pair (i, j) is
+ * related by the spec's rules; tile t (query rows [t*Br, (t+1)*Br)) keeps
+ * key block c (keys [c*Bc, (c+1)*Bc)) iff at least one related pair lies
+ * in it.  Output (host buffers):
+ *   row_ptr[Tr + 1], Tr = ceil(n_q / Br): row_ptr[0] = 0, nondecreasing;
+ *   col_idx[nnz]: ascending within each tile.
+ * Two-call pattern: pass col_idx = NULL to get *nnz_out only.  If
+ * col_capacity < nnz, returns BSATTN_ERR_CAPACITY with *nnz_out set.
+ * Requirements: 1 <= Br, Bc <= 4096; n_q, n_k >= 1; 0 <= n_valid <= n_k; segments
+ * inside [0, n_valid), non-overlapping and consistent with their grid sizes;
+ * anchors inside [0, n_valid).  Violations return BSATTN_ERR_INVALID_ARG.
+ */
+bsattn_status bsattn_build_block_index(const bsattn_mask_spec* spec, int32_t n_q, int32_t n_k,
+                                       int32_t Br, int32_t Bc, int32_t* row_ptr, int32_t* col_idx,
+                                       int64_t col_capacity, int64_t* nnz_out);
+
+/* Check a host CSR: row_ptr[0] == 0, nondecreasing, row_ptr[Tr] = nnz,
+ * col_idx strictly ascending within each tile and inside [0, Tc). */
+bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t* col_idx,
+                                          int32_t Tr, int32_t Tc);
+
+/* Longest-first launch order for the tiles of a CSR (DiT article section 5.3
+ * point 3: uneven rows unbalance the GPU): order[k] is the tile launched
+ * k-th; ties keep ascending tile index.  Host buffers. */
+bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t* order);
+
+/* ------------------------------------------------------------------------ */
+/* prefill                                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t dtype;          /* BSATTN_BF16 (MFMA path) or BSATTN_FP32 (vector path) for q, k, v, out */
+  const void* q;          /* device [B, Nq, Hq, d] (strides below), d contiguous */
+  const void* k;          /* device [B, Nk, Hkv, d] */
+  const void* v;          /* device [B, Nk, Hkv, d] */
+  void* out;              /* device [B, Nq, Hq, d], written for every row < Nq */
+  int32_t B, Hq, Hkv, Nq, Nk, d; /* d in {64, 128}; Hq % Hkv == 0 */
+  int64_t q_stride[3];    /* element strides for batch, token, head */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  const int32_t* row_ptr; /* device CSR at (Br, Bc), [Tr + 1]; NULL = every block */
+  const int32_t* col_idx; /* device [nnz], ascending per tile */
+  const int32_t* tile_order; /* optional device [Tr] launch order (a permutation); NULL = default
+                                (longest-first for causal, ascending otherwise) */
+  int32_t n_valid;        /* keys >= n_valid are never attended; 0 means Nk */
+  float scale;            /* score scale, e.g. 1/sqrt(d); > 0 */
+  float lambda;           /* 0 = static only; 0 < lambda < 1 = BLASST skipping; else INVALID_ARG */
+  int32_t causal;         /* key j attends query i iff j <= i; requires Nq == Nk */
+  int32_t Br, Bc;         /* bf16: Br = 128, Bc = 64.  fp32: Br in {64, 128}, Bc = 64 */
+  int32_t* tile_counters; /* optional device [B, Hq, Tr, 2] int32: {visited, skipped} blocks */
+  uint8_t* block_state;   /* optional device [B, Hq, Tr, Tc]: the kernel writes 1 (computed) or
+                             2 (skipped) for visited blocks; the caller zero-fills it first */
+} bsattn_prefill_args;
+
+/* Enqueue the prefill on `stream` (a hipStream_t; NULL = default stream).
+ * Validation: pointers non-null and 16-byte aligned, token/head strides
+ * multiples of 8 (bf16) or 4 (fp32) elements, d contiguous; CSR pointers
+ * both set or both NULL (the CSR itself is not read on the host: call
+ * bsattn_validate_block_index on the host copy).  Returns BSATTN_ERR_HIP
+ * if the launch fails. */
+bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* decode (one new query token per sequence, split-KV + combine)              */
+/* BLASST notes section 4.2: the decode kernel is memory bound; a skipped     */
+/* block costs the K load and the score, never the V load nor the P.V work.  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const void* q;          /* device bf16 [B, Hq, d]; query of the token at position L-1 */
+  const void* k_cache;    /* device bf16 [B, Lmax, Hkv, d] */
+  const void* v_cache;    /* device bf16 [B, Lmax, Hkv, d] */
+  void* out;              /* device bf16 [B, Hq, d] */
+  int32_t B, Hq, Hkv, L, Lmax, d; /* 1 <= L <= Lmax; d in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8} */
+  int64_t q_stride[2];    /* batch, head (elements) */
+  int64_t kv_stride[3];   /* batch, token, head (elements), shared by k_cache and v_cache */
+  int64_t o_stride[2];    /* batch, head */
+  float scale;
+  float lambda;           /* [0, 1) */
+  int32_t Bc;             /* 64 */
+  int32_t num_splits;     /* splits per (sequence, K/V head); 0 = automatic.  Never changes results
+                             beyond float rounding order; never changes the skip set */
+  void* workspace;        /* device, >= bsattn_decode_workspace_size(...) bytes, 256-byte aligned */
+  size_t workspace_bytes;
+  int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks */
+  uint8_t* block_state;   /* optional device [B, Hkv, Tc]: 1 computed, 2 skipped */
+} bsattn_decode_args;
+
+/* Workspace bytes for a decode call with these sizes (num_splits as in the args). */
+size_t bsattn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
+                                    int32_t Bc, int32_t num_splits);
+
+/* Splits per (sequence, K/V head) a call with these sizes would use. */
+int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
+                                 int32_t Bc, int32_t num_splits);
+
+/* Enqueue the decode (split kernel, then the combine kernel) on `stream`. */
+bsattn_status bsattn_decode_fwd(const bsattn_decode_args* args, void* stream);
+
+/* Read back the decode workspace health word after the stream has finished
+ * (host call, synchronous copy): 0 = fine, else a kernel-side wait timed out
+ * and the output of that call is not valid. */
+bsattn_status bsattn_decode_check(const void* workspace, int32_t* health_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

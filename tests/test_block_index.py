@@ -1,0 +1,119 @@
+"""The C++ block-index builder against the oracle's block mask (host code, CPU only)."""
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_flash_amd as bsa
+from oracle import masks as M
+from workloads import get_config
+from workloads.configs import MaskSpec, Segment, SEG_FULL, SEG_BLOCKWIN, SEG_IMAGE2D, SEG_VIDEO3D, \
+    dit_image_text_spec, video_text_spec
+
+from test_oracle_masks import SMALL_SPECS
+
+
+def _csr_equal(spec, n, Br, Bc):
+    rp, ci = bsa.build_block_index(spec, n, n, Br, Bc)
+    tm = M.tile_mask(spec, n, n, Br, Bc)
+    orp, oci = M.csr_from_tile_mask(tm)
+    assert np.array_equal(rp, orp)
+    assert np.array_equal(ci, oci)
+    bsa.validate_block_index(rp, ci, -(-n // Bc))
+    return rp, ci
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_SPECS))
+@pytest.mark.parametrize("tiles", [(16, 16), (32, 16), (24, 8), (128, 64), (7, 5)])
+def test_small_specs(name, tiles):
+    spec = SMALL_SPECS[name]
+    _csr_equal(spec, spec.n_valid + 13, *tiles)
+
+
+def test_cfg1_and_cfg2_full():
+    c1 = get_config("cfg1")
+    _csr_equal(c1.mask, c1.N, 64, 64)
+    c2 = get_config("cfg2")
+    rp, ci = _csr_equal(c2.mask, c2.N, 128, 64)
+    assert rp[-1] == 640
+    rp64, _ = _csr_equal(c2.mask, c2.N, 64, 64)
+    assert rp64[-1] == 1160
+
+
+def test_cfg3_sampled_tiles_and_counts():
+    c3 = get_config("cfg3")
+    rp, ci = bsa.build_block_index(c3.mask, c3.N, c3.N, 128, 64)
+    assert rp[-1] == 13839                   # kept tile-blocks; 97.4% sparse of 515 x 1030
+    Tr, Tc = 515, 1030
+    assert rp.size == Tr + 1
+    bsa.validate_block_index(rp, ci, Tc)
+    rng = np.random.default_rng(0)
+    tiles = sorted(set([0, 1, 31, 32, 33, 255, 511, 512, 513, 514] + list(rng.integers(0, Tr, 12))))
+    ref = M.tile_mask_rows(c3.mask, c3.N, c3.N, 128, 64, tiles)
+    for a, t in enumerate(tiles):
+        assert np.array_equal(ci[rp[t]:rp[t + 1]], np.nonzero(ref[a])[0]), t
+    assert rp[513] - rp[512] == 1029         # the anchor tile sees every valid block
+    assert not (ci == 1029).any()            # the all-padding key block is never kept
+
+
+def test_random_specs_against_oracle():
+    rng = np.random.default_rng(5)
+    for trial in range(25):
+        W = int(rng.integers(3, 9))
+        H = int(rng.integers(2, 6))
+        F = int(rng.integers(1, 4))
+        text = int(rng.integers(1, 30))
+        nv = F * H * W + text
+        segs = (Segment(SEG_VIDEO3D, 0, F * H * W, frames=F, grid_h=H, grid_w=W, radius=int(rng.integers(0, 3)),
+                        t_radius=int(rng.integers(0, 3)), unit=int(rng.integers(1, W * H + 1))),
+                Segment(SEG_FULL, F * H * W, text))
+        na = int(rng.integers(0, 4))
+        spec = MaskSpec(n_valid=nv, segments=segs, anchor_start=F * H * W, anchor_len=min(na, text))
+        n = nv + int(rng.integers(0, 20))
+        Br, Bc = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+        _csr_equal(spec, n, Br, Bc)
+
+
+def test_capacity_and_spec_errors():
+    c1 = get_config("cfg1")
+    lib = bsa.library()
+    import ctypes as C
+    from block_sparse_attention_flash_amd import _abi
+    cs, keep = bsa._c_spec(c1.mask)
+    rp = np.zeros(9, np.int32)
+    ci = np.zeros(4, np.int32)
+    nnz = C.c_int64(0)
+    st = lib.bsattn_build_block_index(C.byref(cs), 512, 512, 64, 64, rp.ctypes.data, ci.ctypes.data, 4, C.byref(nnz))
+    assert st == _abi.BSATTN_ERR_CAPACITY and nnz.value == 22
+    bad = [
+        MaskSpec(n_valid=600, segments=c1.mask.segments),                                  # n_valid > n_k
+        MaskSpec(n_valid=512, segments=(Segment(SEG_FULL, 0, 300), Segment(SEG_FULL, 200, 100))),  # overlap
+        MaskSpec(n_valid=512, segments=(Segment(SEG_IMAGE2D, 0, 100, grid_h=8, grid_w=8),)),       # 100 != 64
+        MaskSpec(n_valid=512, segments=(Segment(9, 0, 10),)),                              # unknown kind
+        MaskSpec(n_valid=512, segments=(Segment(SEG_BLOCKWIN, 0, 10, unit=0),)),           # unit 0
+        MaskSpec(n_valid=512, segments=(), anchor_start=500, anchor_len=20),               # anchors past n_valid
+    ]
+    for spec in bad:
+        with pytest.raises(bsa.BsattnError) as e:
+            bsa.build_block_index(spec, 512, 512, 64, 64)
+        assert e.value.status == _abi.BSATTN_ERR_INVALID_ARG
+
+
+def test_validate_rejects_malformed_csr():
+    ok_rp = np.array([0, 2, 3], np.int32)
+    ok_ci = np.array([0, 3, 1], np.int32)
+    bsa.validate_block_index(ok_rp, ok_ci, 4)
+    cases = [
+        (np.array([1, 2, 3], np.int32), ok_ci),        # row_ptr[0] != 0
+        (np.array([0, 2, 1], np.int32), ok_ci),        # decreasing
+        (ok_rp, np.array([0, 4, 1], np.int32)),        # out of range
+        (ok_rp, np.array([3, 0, 1], np.int32)),        # not ascending
+        (ok_rp, np.array([0, 0, 1], np.int32)),        # duplicate
+    ]
+    for rp, ci in cases:
+        with pytest.raises(bsa.BsattnError):
+            bsa.validate_block_index(rp, ci, 4)
+
+
+def test_tile_order_lpt():
+    rp = np.array([0, 2, 7, 8, 13, 13], np.int32)   # counts 2, 5, 1, 5, 0
+    assert bsa.tile_order_lpt(rp).tolist() == [1, 3, 0, 2, 4]

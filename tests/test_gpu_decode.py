@@ -1,0 +1,116 @@
+"""GPU parity of bsattn_decode_fwd (split kernel + combine, through the C ABI) against the float64 oracle."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flash_amd as bsa
+from oracle import attention as A
+from workloads import get_config, gen_decode_inputs, gen_decode_sequence
+from workloads.configs import DecodeWorkload
+
+from _parity import MARGIN, compare_out
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[gpu-decode] {msg}", file=sys.stderr, flush=True)
+
+
+def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None):
+    B, Hq, d = q.shape
+    Hkv = kc.shape[2]
+    L = kc.shape[1] if L is None else L
+    Tc = -(-L // 64)
+    ws = torch.empty(bsa.decode_workspace_size(B, Hq, Hkv, L, d, 64, num_splits), dtype=torch.uint8, device=DEV)
+    state = torch.zeros((B, Hkv, Tc), dtype=torch.uint8, device=DEV)
+    counters = torch.full((B, Hkv, 2), -1, dtype=torch.int32, device=DEV)
+    out = bsa.decode_fwd(q, kc, vc, L=L, scale=cfg.scale, lam=cfg.lam if lam is None else lam,
+                         num_splits=num_splits, workspace=ws, counters=counters, block_state=state)
+    torch.cuda.synchronize()
+    assert bsa.decode_check(ws) == 0, "decode look-back wait timed out"
+    return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
+
+
+def check_sequence(q, k, v, out, st, cnt, b, L, scale, lam, groups=None):
+    """q [Hq, d], k/v [L, Hkv, d] host copies of sequence b."""
+    Hq = q.shape[0]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    ref, skip, margin = A.decode_sequence(q, k[:L], v[:L], 64, scale, lam, "closed_form", groups=groups)
+    tot = [0, 0]
+    for g in (range(Hkv) if groups is None else groups):
+        gs = st[b, g] == 2
+        assert np.all(st[b, g] != 0), "every block of the sequence is visited"
+        excused = np.abs(margin[g]) <= MARGIN
+        bad = (gs != skip[g]) & ~excused
+        assert not bad.any(), f"skip set differs b{b} g{g}: {np.nonzero(bad)[0]} margins {margin[g][bad]}"
+        r = ref[g * G:(g + 1) * G]
+        if ((gs != skip[g]) & excused).any():
+            force = {int(i): bool(gs[i]) for i in np.nonzero((gs != skip[g]) & excused)[0]}
+            r, _, _ = A.decode_group(q[g * G:(g + 1) * G], k[:L, g], v[:L, g], 64, scale, lam, "closed_form", force)
+        assert cnt[b, g, 0] == st.shape[2] and cnt[b, g, 1] == int(gs.sum())
+        compare_out(A.as_f64(out[b, g * G:(g + 1) * G]), r, False, f"decode b{b} g{g}")
+        tot[0] += gs.size
+        tot[1] += int(gs.sum())
+    return tot
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (1, 64), (2, 128), (8, 64)])
+def test_decode_small_all_splits(G, d):
+    Hkv = 2
+    L = 3000                                   # ragged last block
+    cfg = DecodeWorkload(name="s", description="", B=2, Hq=G * Hkv, Hkv=Hkv, L=L, d=d, Bc=64, lam=40.0 / L, seed=21)
+    _say(f"decode small G{G} d{d} L{L}")
+    q, kc, vc = gen_decode_inputs(cfg)
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    states = []
+    for S in (0, 1, 3, 7, 47):
+        _say(f"  num_splits {S}")
+        out, st, cnt = run_decode(cfg, qd, kd, vd, num_splits=S)
+        for b in range(cfg.B):
+            check_sequence(q[b], kc[b], vc[b], out, st, cnt, b, L, cfg.scale, cfg.lam)
+        states.append(st)
+    for st in states[1:]:
+        assert np.array_equal(st, states[0]), "skip set depends on the split count"
+
+
+def test_decode_lengths_and_lambda0():
+    cfg = DecodeWorkload(name="s", description="", B=3, Hq=8, Hkv=2, L=5000, d=128, Bc=64, lam=0.0, seed=22)
+    q, kc, vc = gen_decode_inputs(cfg)
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    for L in (1, 63, 64, 65, 4097, 5000):
+        for lam in (0.0, 40.0 / L if L > 40 else 0.5):
+            _say(f"decode L{L} (Lmax 5000) lambda {lam}")
+            out, st, cnt = run_decode(cfg, qd, kd, vd, L=L, lam=lam)
+            for b in range(cfg.B):
+                check_sequence(q[b], kc[b], vc[b], out, st, cnt, b, L, cfg.scale, lam)
+            if lam == 0.0:
+                assert (st == 1).all()
+
+
+def test_cfg5_full_size_sampled():
+    cfg = get_config("cfg5")
+    _say("cfg5 bf16 B32 Hq32 Hkv8 L131072 d128 lambda 40/L")
+    q, kc, vc = gen_decode_inputs(cfg, device=DEV)
+    out, st, cnt = run_decode(cfg, q, kc, vc)
+    skipped = int(cnt[..., 1].sum())
+    total = int(cnt[..., 0].sum())
+    _say(f"  skipped {skipped} of {total} blocks ({100.0 * skipped / total:.1f}%)")
+    assert total == 32 * 8 * 2048
+    for b in (0, 17, 31):
+        _say(f"  oracle on sequence {b}")
+        check_sequence(q[b].cpu(), kc[b].cpu(), vc[b].cpu(), out, st, cnt, b, cfg.L, cfg.scale, cfg.lam)
+
+
+def test_decode_deterministic():
+    cfg = DecodeWorkload(name="s", description="", B=4, Hq=32, Hkv=8, L=20000, d=128, Bc=64, lam=40 / 20000, seed=23)
+    _say("decode determinism")
+    q, kc, vc = (x.to(DEV) for x in gen_decode_inputs(cfg))
+    a = run_decode(cfg, q, kc, vc)
+    b = run_decode(cfg, q, kc, vc)
+    assert torch.equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])

@@ -1,0 +1,219 @@
+"""GPU parity of bsattn_prefill_fwd (through the C ABI) against the float64 oracle."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flash_amd as bsa
+from oracle import masks as M
+from workloads import get_config, gen_prefill_inputs
+from workloads.configs import PrefillWorkload, dit_image_text_spec, video_text_spec
+
+from _parity import check_prefill_tile, compare_out
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[gpu-prefill] {msg}", file=sys.stderr, flush=True)
+
+
+def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None):
+    """Launch through the binding; returns host copies of out, block_state, counters."""
+    Br = cfg.Br if Br is None else Br
+    B, N, Hq, d = q.shape
+    Tr, Tc = -(-N // Br), -(-N // cfg.Bc)
+    state = torch.zeros((B, Hq, Tr, Tc), dtype=torch.uint8, device=DEV)
+    counters = torch.full((B, Hq, Tr, 2), -1, dtype=torch.int32, device=DEV)
+    rp = ci = od = None
+    if csr is not None:
+        rp = torch.from_numpy(csr[0]).to(DEV)
+        ci = torch.from_numpy(csr[1]).to(DEV)
+    if order is not None:
+        od = torch.from_numpy(order).to(DEV)
+    out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam if lam is None else lam, causal=cfg.causal,
+                          Br=Br, Bc=cfg.Bc, row_ptr=rp, col_idx=ci, tile_order=od, n_valid=cfg.n_valid,
+                          tile_counters=counters, block_state=state)
+    torch.cuda.synchronize()
+    return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
+
+
+def _small(name, **kw):
+    base = dict(name=name, description="", dtype="bf16", B=2, Hq=4, Hkv=2, N=300, d=128, Br=128, Bc=64,
+                causal=False, lam=0.0, mask=None, seed=101, generator="iid")
+    base.update(kw)
+    return PrefillWorkload(**base)
+
+
+# ---------------------------------------------------------------------------- static
+
+def test_cfg1_fp32_full():
+    cfg = get_config("cfg1")
+    _say("cfg1 fp32 B1 H2 N512 d64 window +-1 block")
+    q, k, v = gen_prefill_inputs(cfg)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr)
+    for h in range(cfg.Hq):
+        for t in range(cfg.N // cfg.Br):
+            check_prefill_tile(q, k, v, out, st, cnt, 0, h, t, Br=64, Bc=64, scale=cfg.scale, causal=False,
+                               lam=0.0, n_valid=cfg.N, row_ptr=csr[0], col_idx=csr[1], fp32=True)
+    assert (st != 0).sum() == 2 * 22
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_static_small_ragged(d):
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13                                # 309 tokens: 3 tiles, ragged tail, padding keys
+    cfg = _small("small", N=n, d=d, Hq=4, Hkv=4, mask=spec, generator="iid_offset")
+    _say(f"bf16 static small N{n} d{d}")
+    q, k, v = gen_prefill_inputs(cfg)
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, order=bsa.tile_order_lpt(csr[0]))
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            for t in range(3):
+                check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
+                                   lam=0.0, n_valid=spec.n_valid, row_ptr=csr[0], col_idx=csr[1])
+
+
+def test_cfg2_full():
+    cfg = get_config("cfg2")
+    _say("cfg2 bf16 B2 H16 N4352 d64 image+text mask, all heads, all tiles")
+    q, k, v = gen_prefill_inputs(cfg)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, order=bsa.tile_order_lpt(csr[0]))
+    assert (st != 0).sum() == cfg.B * cfg.Hq * 640
+    errs = []
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            for t in range(34):
+                check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
+                                   lam=0.0, n_valid=cfg.N, row_ptr=csr[0], col_idx=csr[1], method="two_pass")
+
+
+def test_cfg3_full_size_sampled():
+    cfg = get_config("cfg3")
+    _say("cfg3 bf16 B1 H24 N65920 d128 video mask, sampled heads/tiles")
+    q, k, v = gen_prefill_inputs(cfg, device=DEV)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    out, st, cnt = run_prefill(cfg, q, k, v, csr=csr, order=bsa.tile_order_lpt(csr[0]))
+    assert int((st != 0).sum()) == cfg.Hq * 13839
+    # exact visited set for every head and tile
+    rp, ci = csr
+    for h in (0, 7, 23):
+        for t in range(515):
+            vis = np.zeros(1030, bool)
+            vis[ci[rp[t]:rp[t + 1]]] = True
+            assert np.array_equal(st[0, h, t] != 0, vis)
+    # outputs on sampled tiles, including the anchor tile and the padded last tile
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    for h in (0, 23):
+        for t in (0, 1, 100, 256, 511, 512, 514):
+            check_prefill_tile(qh, kh, vh, out, st, cnt, 0, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
+                               lam=0.0, n_valid=cfg.mask.n_valid, row_ptr=rp, col_idx=ci, method="two_pass",
+                               rows_limit=cfg.mask.n_valid)
+
+
+# ---------------------------------------------------------------------------- causal / BLASST
+
+@pytest.mark.parametrize("gen,lam", [("concentrated", 0.0), ("concentrated", 0.04), ("sink", 0.3), ("sink", 0.7)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_gqa_dynamic_small(gen, lam, d):
+    cfg = _small("causal", N=1000, d=d, Hq=8, Hkv=2, causal=True, lam=lam, generator=gen, seed=4)
+    _say(f"bf16 causal GQA 8/2 N1000 d{d} {gen} lambda {lam}")
+    q, k, v = gen_prefill_inputs(cfg)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV))
+    tot = [0, 0, 0]
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            for t in range(8):
+                r = check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale, causal=True,
+                                       lam=lam, n_valid=cfg.N)
+                tot = [x + y for x, y in zip(tot, r)]
+    _say(f"  visited {tot[0]} skipped {tot[1]} excused {tot[2]}")
+    if gen == "sink" and lam >= 0.3:
+        assert tot[1] > 0           # the skip path is exercised
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+def test_fp32_causal_dynamic_csr(lam):
+    spec = video_text_spec(frames=3, grid=8, text=20, radius=1, t_radius=1, anchors=4, unit=8)
+    n = spec.n_valid
+    cfg = _small("f32", dtype="fp32", N=n, d=64, Hq=4, Hkv=2, causal=True, lam=lam, mask=spec,
+                 generator="sink", Br=64)
+    _say(f"fp32 causal csr dynamic lambda {lam}")
+    q, k, v = gen_prefill_inputs(cfg)
+    csr = bsa.build_block_index(spec, n, n, 64, 64)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            for t in range(-(-n // 64)):
+                check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=64, Bc=64, scale=cfg.scale, causal=True,
+                                   lam=lam, n_valid=n, row_ptr=csr[0], col_idx=csr[1], fp32=True)
+
+
+def test_bf16_causal_with_csr():
+    spec = dit_image_text_spec(grid=16, text=64, radius=3, anchors=8, unit=16)
+    n = spec.n_valid
+    cfg = _small("csr_causal", N=n, d=128, Hq=4, Hkv=1, causal=True, lam=0.5, mask=spec, generator="sink")
+    _say("bf16 causal + CSR + dynamic")
+    q, k, v = gen_prefill_inputs(cfg)
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            for t in range(-(-n // 128)):
+                check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale, causal=True,
+                                   lam=0.5, n_valid=n, row_ptr=csr[0], col_idx=csr[1])
+
+
+def test_cfg4_full_size_sampled():
+    cfg = get_config("cfg4")
+    _say("cfg4 bf16 causal GQA 32/8 L32768 d128 lambda 40/L, sampled heads/tiles")
+    q, k, v = gen_prefill_inputs(cfg, device=DEV)
+    out, st, cnt = run_prefill(cfg, q, k, v)
+    tr = 256
+    # visited sets of every head/tile: blocks 0..2t+1
+    vis_expected = (np.arange(512)[None, :] <= (2 * np.arange(tr) + 1)[:, None])
+    assert np.array_equal(st[0, 0] != 0, vis_expected) and np.array_equal(st[0, 31] != 0, vis_expected)
+    c = cnt[0].reshape(-1, 2)
+    assert c[:, 0].sum() == 32 * sum(2 * t + 2 for t in range(tr))
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    for h in (0, 31):
+        for t in (0, 1, 77, 200, 255):
+            check_prefill_tile(qh, kh, vh, out, st, cnt, 0, h, t, Br=128, Bc=64, scale=cfg.scale, causal=True,
+                               lam=cfg.lam, n_valid=cfg.N)
+    _say(f"  cfg4 skipped {int(c[:, 1].sum())} of {int(c[:, 0].sum())} visited blocks")
+
+
+def test_deterministic_repeat():
+    cfg = _small("det", N=700, d=128, Hq=8, Hkv=2, causal=True, lam=0.5, generator="sink")
+    _say("determinism")
+    q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+    o1, s1, c1 = run_prefill(cfg, q, k, v)
+    o2, s2, c2 = run_prefill(cfg, q, k, v)
+    assert torch.equal(o1, o2) and np.array_equal(s1, s2) and np.array_equal(c1, c2)
+
+
+def test_strided_views():
+    """q/k/v as non-contiguous views of a packed [B, N, 3, H, d] tensor, output into a strided view."""
+    B, N, H, d = 1, 260, 2, 64
+    g = torch.Generator().manual_seed(3)
+    qkv = torch.randn((B, N, 3, H, d), generator=g).to(torch.bfloat16)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    cfg = _small("strided", N=N, d=d, Hq=H, Hkv=H)
+    _say("strided views")
+    qd = qkv.to(DEV)
+    outbig = torch.zeros((B, N, H, 2 * d), dtype=torch.bfloat16, device=DEV)
+    out = outbig[..., :d]
+    bsa.prefill_fwd(qd[:, :, 0], qd[:, :, 1], qd[:, :, 2], out=out, Br=128, Bc=64)
+    torch.cuda.synchronize()
+    from oracle import attention as A
+    for h in range(H):
+        ref = A.masked_attention(q[0, :, h], k[0, :, h], v[0, :, h], np.ones((N, N), bool), 1 / math.sqrt(d))
+        compare_out(A.as_f64(out[0, :, h].cpu()), ref, False, f"strided h{h}")
+    assert torch.all(outbig[..., d:] == 0)

@@ -24,6 +24,8 @@ Generator readings (the workload text names them, the pages do not):
   (prefill) or over the G heads of the single decode step.
 * cfg2 offset: one random direction per head, scaled to norm 2, added to
   every Q, K and V row of that head.
+* "sink" (test recipe for the skip path): every query gets 4 w and the first
+  64 keys get 10 w, w one random unit direction shared by all heads.
 """
 
 from __future__ import annotations
@@ -91,6 +93,15 @@ def gen_prefill_inputs(cfg: PrefillWorkload, device="cpu", B=None, N=None):
         mq = q.view(B, N, Hkv, G, d).mean(dim=(1, 3))          # [B, Hkv, d]
         ns = min(64, N)
         k[:, :ns] += 4.0 * mq[:, None, :, :]
+    elif cfg.generator == "sink":
+        # a shared query direction w (norm 4) and a sink of 64 keys along w
+        # (norm 10): scores against the sink exceed the others by ~40*scale,
+        # so whole key blocks fall below the BLASST threshold
+        w = _randn((d,), cfg.seed, _TAG_OFF, 0, dev)
+        w = w / w.norm()
+        q += 4.0 * w
+        ns = min(64, N)
+        k[:, :ns] += 10.0 * w
     elif cfg.generator != "iid":
         raise ValueError(cfg.generator)
     dt = _store_dtype(cfg)
