@@ -265,6 +265,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the kernels need no collectives; "
@@ -283,6 +285,15 @@ def main(argv=None) -> int:
         return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep)
 
     torch.cuda.synchronize()
+    if a.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB (reads 1 GiB, writes 1 GiB each)")
+        del src, dst
+        torch.cuda.empty_cache()
     prim = run(a.workload, keep=not a.no_cpu_baseline)
     cpu = None
     if not a.no_cpu_baseline and "_inputs" in prim:
