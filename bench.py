@@ -92,7 +92,7 @@ def time_launches(fn, steps: int, warmup: int):
 
 # ---------------------------------------------------------------------------- prefill
 
-def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool = False):
+def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool = False, use_schedule: bool = True):
     import torch
     import block_sparse_attention_flash_amd as bsa
     from workloads import get_config, gen_prefill_inputs
@@ -102,20 +102,28 @@ def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool =
     log(f"{name}: generating inputs ({cfg.description})")
     q, k, v = gen_prefill_inputs(cfg, device=dev)
     Tr, Tc = -(-cfg.N // cfg.Br), -(-cfg.N // cfg.Bc)
-    rp = ci = order = None
+    rp = ci = order = sched = ws = None
     build_ms = None
     if cfg.mask is not None:
         t0 = time.perf_counter()
         rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
         order_h = bsa.tile_order_lpt(rp_h)
+        if use_schedule:
+            sched = bsa.build_schedule(rp_h, bsa.default_max_blocks_per_item(rp_h, cfg.B, cfg.Hq))
         build_ms = (time.perf_counter() - t0) * 1e3
         rp, ci, order = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, order_h))
+        if sched is not None:
+            sched.to(dev)
+            if sched.n_slots:
+                ws = torch.empty(bsa.prefill_workspace_size(cfg.B, cfg.Hq, cfg.d, sched.n_slots),
+                                 dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     counters = torch.zeros((cfg.B, cfg.Hq, Tr, 2), dtype=torch.int32, device=dev)
 
     def call(cnt=None):
         bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam, causal=cfg.causal, Br=cfg.Br, Bc=cfg.Bc,
-                        row_ptr=rp, col_idx=ci, tile_order=order, n_valid=cfg.n_valid, out=out, tile_counters=cnt)
+                        row_ptr=rp, col_idx=ci, tile_order=order, n_valid=cfg.n_valid, out=out, tile_counters=cnt,
+                        schedule=sched, workspace=ws)
 
     call(counters)                       # untimed: counts visited / skipped blocks
     torch.cuda.synchronize()
@@ -145,6 +153,8 @@ def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool =
         "blocks": {"visited": visited, "skipped": skipped, "computed": visited - skipped,
                    "tile_blocks_total": cfg.B * cfg.Hq * Tr * Tc},
         "lambda": cfg.lam, "block_index_build_ms": build_ms,
+        "schedule": None if sched is None else {"items": sched.n_items, "cut_tiles": sched.n_merges,
+                                                "partial_slots": sched.n_slots},
         "config": {"workload": f"{name}: {cfg.description}", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
                    "Br": cfg.Br, "Bc": cfg.Bc, "causal": cfg.causal, "lambda": cfg.lam, "dtype": cfg.dtype},
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": achieved,
@@ -264,6 +274,7 @@ def main(argv=None) -> int:
     ap.add_argument("--also", default="cfg3,cfg4,cfg5", help="comma list of further workloads ('' for none)")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true", help="one work-group per tile (no long-tile cutting)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -282,7 +293,7 @@ def main(argv=None) -> int:
     def run(name, keep=False):
         if name == "cfg5":
             return run_decode_workload(name, a.steps, a.warmup)
-        return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep)
+        return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep, use_schedule=not a.no_schedule)
 
     torch.cuda.synchronize()
     if a.calibrate_copy:

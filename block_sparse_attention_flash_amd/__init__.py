@@ -11,6 +11,8 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``build_block_index(spec, n_q, n_k, Br, Bc)`` -> (row_ptr, col_idx) int32 numpy
 * ``validate_block_index(row_ptr, col_idx, Tc)``
 * ``tile_order_lpt(row_ptr)`` -> int32 numpy launch order
+* ``build_schedule(row_ptr, max_blocks_per_item)`` -> Schedule (host arrays, counts)
+* ``prefill_workspace_size(B, Hq, d, n_slots)``
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
 * ``decode_workspace_size(...)``, ``decode_num_splits(...)``, ``decode_check(workspace)``
@@ -28,7 +30,7 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
-    "prefill_fwd", "decode_fwd", "decode_workspace_size", "decode_num_splits", "decode_check",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_fwd", "decode_fwd", "decode_workspace_size", "decode_num_splits", "decode_check",
 ]
 
 
@@ -121,6 +123,53 @@ def tile_order_lpt(row_ptr):
     return order
 
 
+class Schedule:
+    """Host arrays of bsattn_build_schedule plus their device copies (``to``)."""
+
+    def __init__(self, items, merges, n_slots):
+        self.items, self.merges, self.n_slots = items, merges, int(n_slots)
+        self.d_items = self.d_merges = None
+
+    @property
+    def n_items(self) -> int:
+        return self.items.shape[0]
+
+    @property
+    def n_merges(self) -> int:
+        return self.merges.shape[0]
+
+    def to(self, device):
+        torch = _torch()
+        self.d_items = torch.from_numpy(self.items.reshape(-1)).to(device)
+        self.d_merges = torch.from_numpy(self.merges.reshape(-1)).to(device) if self.n_merges else None
+        return self
+
+
+def default_max_blocks_per_item(row_ptr, B: int, Hq: int, slots: int = 512) -> int:
+    """Chunk bound: half the mean work per concurrent work-group slot, at least 16 blocks."""
+    total = int(row_ptr[-1]) * B * Hq
+    return max(16, -(-total // (2 * slots)))
+
+
+def build_schedule(row_ptr, max_blocks_per_item: int) -> Schedule:
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    Tr = row_ptr.size - 1
+    ni, nm, ns = C.c_int32(0), C.c_int32(0), C.c_int32(0)
+    lib = library()
+    _check(lib.bsattn_build_schedule(row_ptr.ctypes.data, Tr, int(max_blocks_per_item), None, 0, None, 0,
+                                     C.byref(ni), C.byref(nm), C.byref(ns)))
+    items = np.zeros((ni.value, 4), np.int32)
+    merges = np.zeros((max(1, nm.value), 3), np.int32)
+    _check(lib.bsattn_build_schedule(row_ptr.ctypes.data, Tr, int(max_blocks_per_item), items.ctypes.data,
+                                     ni.value, merges.ctypes.data, merges.shape[0], C.byref(ni), C.byref(nm),
+                                     C.byref(ns)))
+    return Schedule(items, merges[:nm.value].copy(), ns.value)
+
+
+def prefill_workspace_size(B: int, Hq: int, d: int, n_slots: int) -> int:
+    return int(library().bsattn_prefill_workspace_size(B, Hq, d, n_slots))
+
+
 # ---------------------------------------------------------------------------
 # device entry points
 # ---------------------------------------------------------------------------
@@ -143,12 +192,16 @@ def _ptr(t) -> Optional[int]:
 
 def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                 Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
-                out=None, tile_counters=None, block_state=None, stream=None):
+                out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
+                workspace=None, stream=None):
     """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
 
     ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
     ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
-    [B, Hq, Tr, Tc] are optional device outputs.  Returns ``out``."""
+    [B, Hq, Tr, Tc] are optional device outputs.  ``schedule`` (from
+    ``build_schedule``, device copies made with ``.to``) cuts long tiles;
+    its partials go to ``workspace`` (uint8 device tensor, allocated here if
+    None).  Returns ``out``."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
         dt = _abi.BSATTN_BF16
@@ -178,6 +231,17 @@ def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, cau
     a.causal = 1 if causal else 0
     a.Br, a.Bc = int(Br), int(Bc)
     a.tile_counters, a.block_state = _ptr(tile_counters), _ptr(block_state)
+    if schedule is not None:
+        if schedule.d_items is None:
+            schedule.to(q.device)
+        a.sched_items, a.n_items = _ptr(schedule.d_items), schedule.n_items
+        a.sched_merges, a.n_merges, a.n_slots = _ptr(schedule.d_merges), schedule.n_merges, schedule.n_slots
+        if schedule.n_slots > 0:
+            if workspace is None:
+                workspace = torch.empty(prefill_workspace_size(B, Hq, d, schedule.n_slots), dtype=torch.uint8,
+                                        device=q.device)
+            a.workspace = _ptr(workspace)
+            a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     _check(library().bsattn_prefill_fwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
     return out
 

@@ -21,7 +21,7 @@ BSATTN_FP32 = 1
 EXPORTED = (
     "bsattn_status_string", "bsattn_last_error", "bsattn_version",
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
-    "bsattn_prefill_fwd",
+    "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_fwd", "bsattn_decode_check",
 )
 
@@ -47,7 +47,10 @@ class PrefillArgs(C.Structure):
                 ("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("tile_order", C.c_void_p),
                 ("n_valid", C.c_int32), ("scale", C.c_float), ("lam", C.c_float), ("causal", C.c_int32),
                 ("Br", C.c_int32), ("Bc", C.c_int32),
-                ("tile_counters", C.c_void_p), ("block_state", C.c_void_p)]
+                ("tile_counters", C.c_void_p), ("block_state", C.c_void_p),
+                ("sched_items", C.c_void_p), ("n_items", C.c_int32), ("sched_merges", C.c_void_p),
+                ("n_merges", C.c_int32), ("n_slots", C.c_int32), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t)]
 
 
 class DecodeArgs(C.Structure):
@@ -60,7 +63,9 @@ class DecodeArgs(C.Structure):
                 ("counters", C.c_void_p), ("block_state", C.c_void_p)]
 
 
-def load(path: str = LIB_PATH) -> C.CDLL:
+def load(path: str = None) -> C.CDLL:
+    """Load libbsattn.so (``BSATTN_LIB`` overrides the in-tree path)."""
+    path = path or os.environ.get("BSATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m block_sparse_attention_flash_amd.build` "
@@ -78,6 +83,12 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.bsattn_validate_block_index.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32]
     lib.bsattn_tile_order_lpt.restype = C.c_int
     lib.bsattn_tile_order_lpt.argtypes = [C.c_void_p, C.c_int32, C.c_void_p]
+    lib.bsattn_build_schedule.restype = C.c_int
+    lib.bsattn_build_schedule.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                          C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                          C.POINTER(C.c_int32)]
+    lib.bsattn_prefill_workspace_size.restype = C.c_size_t
+    lib.bsattn_prefill_workspace_size.argtypes = [C.c_int32] * 4
     lib.bsattn_prefill_fwd.restype = C.c_int
     lib.bsattn_prefill_fwd.argtypes = [C.POINTER(PrefillArgs), C.c_void_p]
     lib.bsattn_decode_workspace_size.restype = C.c_size_t

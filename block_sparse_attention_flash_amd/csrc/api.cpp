@@ -65,6 +65,17 @@ DecodeWorkspace decode_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int3
   return w;
 }
 
+PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int32_t n_slots) {
+  PrefillWorkspace w{};
+  const size_t units = (size_t)n_slots * B * Hq;
+  size_t off = 0;
+  w.o = off;   off = align256(off + units * 128 * (size_t)d * sizeof(float));
+  w.ml = off;  off = align256(off + units * 128 * 2 * sizeof(float));
+  w.cnt = off; off = align256(off + units * 2 * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
 // Largest split (in Bc-blocks) whose scores fit the kernel's LDS score buffer
 // (8192 floats) for G query heads.
 static int32_t max_blocks_per_split(int32_t G) {
@@ -153,9 +164,37 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   p.Tr = (a->Nq + a->Br - 1) / a->Br;
   p.Tc = (a->Nk + a->Bc - 1) / a->Bc;
   p.tile_counters = a->tile_counters; p.block_state = a->block_state;
-  if ((int64_t)p.B * p.Hq * p.Tr > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  if (a->sched_items) {
+    if (a->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "schedules are implemented for the bf16 path");
+    if (!a->row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a schedule needs the CSR (row_ptr, col_idx)");
+    if (a->n_items < 1) return fail(BSATTN_ERR_INVALID_ARG, "n_items must be >= 1");
+    if (a->n_slots < 0 || a->n_merges < 0 || (a->n_merges > 0) != (a->n_slots > 0) || (a->n_merges > 0 && !a->sched_merges))
+      return fail(BSATTN_ERR_INVALID_ARG, "inconsistent schedule counts (n_merges, n_slots, sched_merges)");
+    if (a->n_slots > 0 && a->lambda > 0.0f)
+      return fail(BSATTN_ERR_UNSUPPORTED, "a schedule that cuts tiles needs lambda == 0 (BLASST decisions span the row)");
+    if (a->n_slots > 0) {
+      const PrefillWorkspace w = prefill_workspace_layout(a->B, a->Hq, a->d, a->n_slots);
+      if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+      if (a->workspace_bytes < w.total)
+        return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
+      char* ws = static_cast<char*>(a->workspace);
+      p.part_o = reinterpret_cast<float*>(ws + w.o);
+      p.part_ml = reinterpret_cast<float*>(ws + w.ml);
+      p.part_cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+    }
+    p.sched_items = a->sched_items; p.n_items = a->n_items;
+    p.sched_merges = a->sched_merges; p.n_merges = a->n_merges; p.n_slots = a->n_slots;
+  }
+  const int64_t units = p.sched_items ? p.n_items : p.Tr;
+  if ((int64_t)p.B * p.Hq * units > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   int e = a->dtype == BSATTN_BF16 ? launch_prefill_bf16(p, stream) : launch_prefill_f32(p, stream);
   return hip_status(e, "prefill launch");
+}
+
+size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n_slots) {
+  if (B < 1 || Hq < 1 || d < 1 || n_slots < 0) return 0;
+  return prefill_workspace_layout(B, Hq, d, n_slots).total;
 }
 
 size_t bsattn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d, int32_t Bc,

@@ -246,6 +246,51 @@ bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t*
   return BSATTN_OK;
 }
 
+bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t max_blocks, int32_t* items,
+                                    int32_t items_capacity, int32_t* merges, int32_t merges_capacity, int32_t* n_items,
+                                    int32_t* n_merges, int32_t* n_slots) {
+  using namespace bsattn;
+  clear_error();
+  if (!row_ptr || Tr < 1 || !n_items || !n_merges || !n_slots)
+    return fail(BSATTN_ERR_INVALID_ARG, "row_ptr / counts NULL or Tr < 1");
+  if (max_blocks < 1) return fail(BSATTN_ERR_INVALID_ARG, "max_blocks_per_item must be >= 1");
+  struct Item { int32_t tile, first, end, slot; };
+  std::vector<Item> it;
+  std::vector<int32_t> mg;
+  int32_t slots = 0;
+  for (int32_t t = 0; t < Tr; ++t) {
+    const int32_t b = row_ptr[t], e = row_ptr[t + 1];
+    if (e < b) return fail(BSATTN_ERR_INVALID_ARG, "row_ptr decreases at tile %d", t);
+    const int32_t n = e - b;
+    if (n <= max_blocks) {
+      it.push_back({t, b, e, -1});
+      continue;
+    }
+    const int32_t k = (n + max_blocks - 1) / max_blocks;  // chunks of near-equal size
+    mg.insert(mg.end(), {t, slots, k});
+    for (int32_t c = 0; c < k; ++c) {
+      const int32_t cb = b + (int32_t)((int64_t)n * c / k), ce = b + (int32_t)((int64_t)n * (c + 1) / k);
+      it.push_back({t, cb, ce, slots + c});
+    }
+    slots += k;
+  }
+  std::stable_sort(it.begin(), it.end(), [](const Item& x, const Item& y) { return (x.end - x.first) > (y.end - y.first); });
+  *n_items = (int32_t)it.size();
+  *n_merges = (int32_t)(mg.size() / 3);
+  *n_slots = slots;
+  if (!items) return BSATTN_OK;
+  if (items_capacity < *n_items || (*n_merges > 0 && (!merges || merges_capacity < *n_merges)))
+    return fail(BSATTN_ERR_CAPACITY, "schedule needs %d items and %d merges", *n_items, *n_merges);
+  for (size_t i = 0; i < it.size(); ++i) {
+    items[4 * i + 0] = it[i].tile;
+    items[4 * i + 1] = it[i].first;
+    items[4 * i + 2] = it[i].end;
+    items[4 * i + 3] = it[i].slot;
+  }
+  if (!mg.empty()) std::memcpy(merges, mg.data(), mg.size() * sizeof(int32_t));
+  return BSATTN_OK;
+}
+
 bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t* order) {
   using namespace bsattn;
   clear_error();

@@ -28,7 +28,12 @@
 // The skip test always uses the true running max.
 //
 // K/V blocks are staged global -> registers -> LDS, double buffered, with
-// one barrier per block (two when the vote is on).  As in the BLASST notes
+// one barrier per block (two when the vote is on).  Two work-groups share a
+// CU, so one group's exponentials overlap the other's MFMAs.
+//
+// Long static tiles can be cut into chunks by a host schedule; a chunk
+// writes its (reference max, row sum, unnormalised O) and a merge kernel
+// combines the chunks (online-softmax rescaling, attention tutorial 4.2).  As in the BLASST notes
 // section 4.1, the prefill still streams V for blocks it skips: prefill is
 // compute bound and the load is issued one block ahead, before the skip
 // decision is known.
@@ -85,8 +90,13 @@ __device__ __forceinline__ void store_block_lds(const u32x4 (&kr)[D / 32], const
   }
 }
 
+// Work-groups per CU the register budget is cut for: three at d = 64 (at most
+// 168 VGPRs), two at d = 128 (at most 256).
+template <int D>
+constexpr int kMinBlocksPerCu = D == 64 ? 3 : 2;
+
 template <int D, bool CAUSAL, bool DYN>
-__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(const PrefillParams p) {
   constexpr int PITCH = Smem<D>::PITCH;
   constexpr int KS = D / 16;  // k-steps of the S MFMA
   constexpr int NTD = D / 32; // 32-wide d tiles of the O MFMA
@@ -101,18 +111,29 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams
   // ---- work item: XCD-aware mapping (WG i runs on XCD i % 8), then
   //      (batch, kv head, tile rank, head in group) with heads innermost so
   //      the G heads sharing K/V run together on one XCD.
+  const int units = p.sched_items ? p.n_items : p.Tr;
   const int G = p.Hq / p.Hkv;
-  const int64_t W = (int64_t)p.B * p.Hq * p.Tr;
+  const int64_t W = (int64_t)p.B * p.Hq * units;
   int64_t wi = blockIdx.x;
   if ((W & 7) == 0) wi = (wi & 7) * (W >> 3) + (wi >> 3);
   const int hh = (int)(wi % G);
   wi /= G;
-  const int rank = (int)(wi % p.Tr);
-  wi /= p.Tr;
+  const int rank = (int)(wi % units);
+  wi /= units;
   const int g = (int)(wi % p.Hkv);
   const int b = (int)(wi / p.Hkv);
   const int h = g * G + hh;
-  const int t = p.tile_order ? p.tile_order[rank] : (CAUSAL ? p.Tr - 1 - rank : rank);
+  int t, e0, e1, slot = -1;
+  if (p.sched_items) {
+    t = p.sched_items[4 * rank + 0];
+    e0 = p.sched_items[4 * rank + 1];
+    e1 = p.sched_items[4 * rank + 2];
+    slot = p.sched_items[4 * rank + 3];
+  } else {
+    t = p.tile_order ? p.tile_order[rank] : (CAUSAL ? p.Tr - 1 - rank : rank);
+    e0 = p.row_ptr ? p.row_ptr[t] : 0;
+    e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
+  }
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
@@ -131,25 +152,22 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams
       qf[ks] = bf16x8{};
   }
 
-  // visited blocks
+  // visited blocks: entries [e0, e1) of the CSR list (or blocks e0..e1-1),
+  // minus blocks wholly above the diagonal
   const int last_row = min(t * BR + BR, p.Nq) - 1;
-  int beg = 0, nblk;
-  const int32_t* cols = nullptr;
-  if (p.row_ptr) {
-    beg = p.row_ptr[t];
-    const int end = p.row_ptr[t + 1];
-    cols = p.col_idx + beg;
-    nblk = end - beg;
-    if (CAUSAL) {  // ascending list: keep entries with j*BC <= last_row
+  const int32_t* cols = p.row_ptr ? p.col_idx + e0 : nullptr;
+  int nblk = e1 - e0;
+  if (CAUSAL) {
+    if (cols) {  // ascending list: keep entries with j*BC <= last_row
       int lo = 0, hi2 = nblk;
       while (lo < hi2) {
         const int mid = (lo + hi2) >> 1;
         if (cols[mid] * BC <= last_row) lo = mid + 1; else hi2 = mid;
       }
       nblk = lo;
+    } else {
+      nblk = max(0, min(nblk, last_row / BC + 1 - e0));
     }
-  } else {
-    nblk = CAUSAL ? min(p.Tc, last_row / BC + 1) : p.Tc;
   }
 
   const float c2 = p.scale * kLog2e;                    // raw score -> log2 units
@@ -164,18 +182,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams
 
   u32x4 kr[D / 32], vr[D / 32];
   if (nblk > 0) {
-    const int j0 = cols ? cols[0] : 0;
+    const int j0 = cols ? cols[0] : e0;
     load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, j0, p.Nk, tid);
     store_block_lds<D>(kr, vr, sm.k[0], sm.v[0], tid);
   }
 
   for (int it = 0; it < nblk; ++it) {
     const int buf = it & 1;
-    const int j = cols ? cols[it] : it;
+    const int j = cols ? cols[it] : e0 + it;
     __syncthreads();  // block it in LDS; everyone is done with block it-1
     const bool more = it + 1 < nblk;
     if (more) {
-      const int jn = cols ? cols[it + 1] : it + 1;
+      const int jn = cols ? cols[it + 1] : e0 + it + 1;
       load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, jn, p.Nk, tid);
     }
     const __bf16* ks = sm.k[buf];
@@ -279,33 +297,117 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const PrefillParams
     if (more) store_block_lds<D>(kr, vr, sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
   }
 
-  // ---- epilogue: O / l, bf16 store
+  // ---- epilogue: O / l, bf16 store (or the partial of a cut tile)
   const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (row_ok) {
-    __bf16* obase = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
+  if (slot < 0) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (row_ok) {
+      __bf16* obase =
+          static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
 #pragma unroll
-    for (int n = 0; n < NTD; ++n) {
+      for (int n = 0; n < NTD; ++n) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dcol = 32 * n + 8 * q4 + 4 * hi;
+          f32x4 v4 = {oacc[n][4 * q4 + 0] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
+                      oacc[n][4 * q4 + 3] * inv};
+          *reinterpret_cast<bf16x4*>(obase + dcol) = __builtin_convertvector(v4, bf16x4);
+        }
+      }
+    }
+    if (p.tile_counters && tid == 0) {
+      int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
+      tc[0] = nblk;
+      tc[1] = skipped;
+    }
+  } else {
+    // partial of a cut tile: unnormalised O relative to m_ref, plus (m_ref, l)
+    const int64_t unit = ((int64_t)slot * p.B + b) * p.Hq + h;
+    const int lrow = wave * 32 + l32;
+    float* po = p.part_o + (unit * BR + lrow) * D;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int dcol = 32 * n + 8 * q4 + 4 * hi;
-        f32x4 v4 = {oacc[n][4 * q4 + 0] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
-                    oacc[n][4 * q4 + 3] * inv};
-        *reinterpret_cast<bf16x4*>(obase + dcol) = __builtin_convertvector(v4, bf16x4);
+        f32x4 v4 = {oacc[n][4 * q4 + 0], oacc[n][4 * q4 + 1], oacc[n][4 * q4 + 2], oacc[n][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(po + 32 * n + 8 * q4 + 4 * hi) = v4;
+      }
+    if (hi == 0) {
+      p.part_ml[(unit * BR + lrow) * 2 + 0] = m_ref;
+      p.part_ml[(unit * BR + lrow) * 2 + 1] = l_tot;
+    }
+    if (tid == 0) {
+      p.part_cnt[unit * 2 + 0] = nblk;
+      p.part_cnt[unit * 2 + 1] = skipped;
+    }
+  }
+}
+
+// Combine the chunk partials of each cut tile: M = max m_s, w_s = 2^((m_s - M) c2),
+// out = sum w_s O_s / sum w_s l_s.  Two threads per query row.
+template <int D>
+__global__ __launch_bounds__(NT) void prefill_merge_kernel(const PrefillParams p) {
+  const int m = blockIdx.x % p.n_merges;
+  const int bh = blockIdx.x / p.n_merges;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int t = p.sched_merges[3 * m + 0];
+  const int s0 = p.sched_merges[3 * m + 1];
+  const int ns = p.sched_merges[3 * m + 2];
+  const int lrow = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int row = t * BR + lrow;
+  const float c2 = p.scale * kLog2e;
+  auto unit = [&](int s) __attribute__((always_inline)) { return ((int64_t)(s0 + s) * p.B + b) * p.Hq + h; };
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(unit(s) * BR + lrow) * 2]);
+  float acc[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) acc[c] = 0.0f;
+  float l = 0.0f;
+  if (M != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const float ms = p.part_ml[(unit(s) * BR + lrow) * 2];
+      if (ms == kNegInf) continue;
+      const float w = fast_exp2((ms - M) * c2);
+      l += w * p.part_ml[(unit(s) * BR + lrow) * 2 + 1];
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + (unit(s) * BR + lrow) * D + half * (D / 2));
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const f32x4 x = src[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(w, x[e], acc[4 * c + e]);
       }
     }
   }
-  if (p.tile_counters && tid == 0) {
+  if (row < p.Nq) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h +
+                half * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      f32x4 v4 = {acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv};
+      *reinterpret_cast<bf16x4*>(o + 4 * c) = __builtin_convertvector(v4, bf16x4);
+    }
+  }
+  if (p.tile_counters && threadIdx.x == 0) {
+    int vis = 0, sk = 0;
+    for (int s = 0; s < ns; ++s) {
+      vis += p.part_cnt[unit(s) * 2];
+      sk += p.part_cnt[unit(s) * 2 + 1];
+    }
     int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
-    tc[0] = nblk;
-    tc[1] = skipped;
+    tc[0] = vis;
+    tc[1] = sk;
   }
 }
 
 template <int D, bool CAUSAL, bool DYN>
 hipError_t launch(const PrefillParams& p, hipStream_t s) {
-  const int64_t grid = (int64_t)p.B * p.Hq * p.Tr;
+  const int64_t units = p.sched_items ? p.n_items : p.Tr;
+  const int64_t grid = (int64_t)p.B * p.Hq * units;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, DYN>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_merges == 0) return e;
+  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)(p.n_merges * p.B * p.Hq)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -127,6 +127,27 @@ bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t*
  * k-th; ties keep ascending tile index.  Host buffers. */
 bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t* order);
 
+/*
+ * Work schedule for a static CSR (same load-imbalance concern): tiles with
+ * more than max_blocks_per_item kept blocks are cut into near-equal chunks of
+ * consecutive CSR entries, each chunk a separate work-group writing a partial
+ * (running max, row sum, unnormalised output) to the prefill workspace; a
+ * merge step then combines the chunks of each cut tile with the online-
+ * softmax rescaling rule (attention tutorial section 4.2).  Exact for lambda
+ * = 0; a schedule that cuts tiles is refused for lambda > 0, whose skip
+ * decisions depend on the whole row (BLASST notes Algorithm 1).
+ *   items  [n_items][4]  {tile, first CSR entry, end CSR entry, slot}; slot = -1
+ *                        means the item writes the output directly; items are
+ *                        ordered longest first
+ *   merges [n_merges][3] {tile, first slot, number of slots}
+ * Two-call pattern: items == NULL returns the counts only.  Host buffers.
+ * max_blocks_per_item >= 1.  Returns BSATTN_ERR_CAPACITY if a buffer is short.
+ */
+bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t max_blocks_per_item,
+                                    int32_t* items, int32_t items_capacity, int32_t* merges,
+                                    int32_t merges_capacity, int32_t* n_items, int32_t* n_merges,
+                                    int32_t* n_slots);
+
 /* ------------------------------------------------------------------------ */
 /* prefill                                                                    */
 /* ------------------------------------------------------------------------ */
@@ -154,7 +175,19 @@ typedef struct {
   int32_t* tile_counters; /* optional device [B, Hq, Tr, 2] int32: {visited, skipped} blocks */
   uint8_t* block_state;   /* optional device [B, Hq, Tr, Tc]: the kernel writes 1 (computed) or
                              2 (skipped) for visited blocks; the caller zero-fills it first */
+  const int32_t* sched_items;  /* optional device copy of bsattn_build_schedule's items (needs the CSR);
+                                  NULL = one work-group per tile (tile_order applies) */
+  int32_t n_items;
+  const int32_t* sched_merges; /* device copy of the schedule's merges (NULL if n_merges == 0) */
+  int32_t n_merges;
+  int32_t n_slots;             /* partial slots of the schedule; > 0 requires lambda == 0 */
+  void* workspace;             /* device, >= bsattn_prefill_workspace_size(B, Hq, d, n_slots) bytes,
+                                  256-byte aligned; unused when n_slots == 0 */
+  size_t workspace_bytes;
 } bsattn_prefill_args;
+
+/* Workspace bytes for a prefill whose schedule has n_slots partial slots. */
+size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n_slots);
 
 /* Enqueue the prefill on `stream` (a hipStream_t; NULL = default stream).
  * Validation: pointers non-null and 16-byte aligned, token/head strides

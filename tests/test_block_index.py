@@ -117,3 +117,54 @@ def test_validate_rejects_malformed_csr():
 def test_tile_order_lpt():
     rp = np.array([0, 2, 7, 8, 13, 13], np.int32)   # counts 2, 5, 1, 5, 0
     assert bsa.tile_order_lpt(rp).tolist() == [1, 3, 0, 2, 4]
+
+
+def test_schedule_covers_every_entry_once():
+    c3 = get_config("cfg3")
+    rp, ci = bsa.build_block_index(c3.mask, c3.N, c3.N, 128, 64)
+    for mx in (1, 7, 64, 5000):
+        sc = bsa.build_schedule(rp, mx)
+        seen = np.zeros(rp[-1], np.int32)
+        tiles_direct = set()
+        lens = []
+        for t, a, b, slot in sc.items:
+            assert rp[t] <= a <= b <= rp[t + 1]
+            assert b - a <= mx
+            seen[a:b] += 1
+            lens.append(b - a)
+            if slot < 0:
+                tiles_direct.add(int(t))
+        assert (seen == 1).all()
+        assert lens == sorted(lens, reverse=True)                  # longest first
+        cut = {int(t) for t, s0, n in sc.merges}
+        assert cut.isdisjoint(tiles_direct) and len(cut | tiles_direct) == 515
+        slots = sorted(int(s) for s in sc.items[:, 3] if s >= 0)
+        assert slots == list(range(sc.n_slots))
+        for t, s0, n in sc.merges:                                 # slots of a cut tile are consecutive
+            assert sorted(int(s) for tt, a, b, s in sc.items if tt == t) == list(range(s0, s0 + n))
+    assert bsa.build_schedule(rp, 5000).n_slots == 0
+
+
+def test_schedule_validation():
+    import ctypes as C
+    from block_sparse_attention_flash_amd import _abi
+    from test_abi import _good_prefill
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_schedule(np.array([0, 3, 1], np.int32), 4)          # decreasing row_ptr
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_schedule(np.array([0, 3], np.int32), 0)             # max_blocks < 1
+    lib = bsa.library()
+    a = _good_prefill()
+    a.sched_items, a.n_items = 0x20000, 4
+    st = lib.bsattn_prefill_fwd(C.byref(a), None)
+    assert st == _abi.BSATTN_ERR_INVALID_ARG                         # schedule without CSR
+    a.row_ptr = a.col_idx = 0x30000
+    a.sched_merges, a.n_merges, a.n_slots = 0x40000, 1, 2
+    a.lam = 0.1
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_UNSUPPORTED   # cut tiles + BLASST
+    a.lam = 0.0
+    a.workspace, a.workspace_bytes = 0x50000, 16
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_CAPACITY
+    a.n_merges = 0
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG   # inconsistent counts
+    assert bsa.prefill_workspace_size(2, 16, 64, 3) >= 3 * 2 * 16 * 128 * 66 * 4

@@ -22,7 +22,7 @@ def _say(msg):
     print(f"[gpu-prefill] {msg}", file=sys.stderr, flush=True)
 
 
-def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None):
+def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedule=None):
     """Launch through the binding; returns host copies of out, block_state, counters."""
     Br = cfg.Br if Br is None else Br
     B, N, Hq, d = q.shape
@@ -37,7 +37,7 @@ def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None):
         od = torch.from_numpy(order).to(DEV)
     out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam if lam is None else lam, causal=cfg.causal,
                           Br=Br, Bc=cfg.Bc, row_ptr=rp, col_idx=ci, tile_order=od, n_valid=cfg.n_valid,
-                          tile_counters=counters, block_state=state)
+                          tile_counters=counters, block_state=state, schedule=schedule)
     torch.cuda.synchronize()
     return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
 
@@ -217,3 +217,41 @@ def test_strided_views():
         ref = A.masked_attention(q[0, :, h], k[0, :, h], v[0, :, h], np.ones((N, N), bool), 1 / math.sqrt(d))
         compare_out(A.as_f64(out[0, :, h].cpu()), ref, False, f"strided h{h}")
     assert torch.all(outbig[..., d:] == 0)
+
+
+@pytest.mark.parametrize("max_blocks", [1, 3, 9, 100])
+def test_schedule_cut_tiles_small(max_blocks):
+    """Tiles cut into chunks (partials + merge) give the same outputs, counters and visited sets."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13
+    for d in (64, 128):
+        cfg = _small("sched", N=n, d=d, Hq=4, Hkv=2, mask=spec, generator="iid_offset")
+        cfg = PrefillWorkload(**{**cfg.__dict__, "Hkv": 4})
+        _say(f"schedule max_blocks {max_blocks} d{d}")
+        q, k, v = gen_prefill_inputs(cfg)
+        csr = bsa.build_block_index(spec, n, n, 128, 64)
+        sched = bsa.build_schedule(csr[0], max_blocks)
+        assert (sched.n_slots > 0) == (int(np.diff(csr[0]).max()) > max_blocks)
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched)
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                for t in range(3):
+                    check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale,
+                                       causal=False, lam=0.0, n_valid=spec.n_valid, row_ptr=csr[0], col_idx=csr[1])
+
+
+def test_cfg3_full_size_schedule():
+    cfg = get_config("cfg3")
+    _say("cfg3 with the default schedule (anchor tile cut into chunks)")
+    q, k, v = gen_prefill_inputs(cfg, device=DEV)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    sched = bsa.build_schedule(csr[0], bsa.default_max_blocks_per_item(csr[0], cfg.B, cfg.Hq))
+    assert sched.n_merges >= 1
+    out, st, cnt = run_prefill(cfg, q, k, v, csr=csr, schedule=sched)
+    assert int((st != 0).sum()) == cfg.Hq * 13839
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    for h in (0, 23):
+        for t in (100, 512, 514):
+            check_prefill_tile(qh, kh, vh, out, st, cnt, 0, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
+                               lam=0.0, n_valid=cfg.mask.n_valid, row_ptr=csr[0], col_idx=csr[1], method="two_pass",
+                               rows_limit=cfg.mask.n_valid)
