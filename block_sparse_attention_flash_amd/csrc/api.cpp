@@ -55,6 +55,7 @@ DecodeWorkspace decode_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int3
   const int32_t G = Hq / Hkv;
   size_t off = 0;
   w.header = off; off = align256(off + 16 * sizeof(int32_t));
+  w.tickets = off; off = align256(off + (size_t)B * Hkv * sizeof(int32_t));
   w.flags = off;  off = align256(off + units * sizeof(int32_t));
   w.agg = off;    off = align256(off + units * 16 * sizeof(float));
   w.incl = off;   off = align256(off + units * 16 * sizeof(float));
@@ -76,11 +77,10 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   return w;
 }
 
-// Largest split (in Bc-blocks) whose scores fit the kernel's LDS score buffer
-// (8192 floats) for G query heads.
+// Largest split (in Bc-blocks): the kernel's skip mask is one 64-bit word.
 static int32_t max_blocks_per_split(int32_t G) {
-  int32_t m = 8192 / (64 * G);
-  return m > 64 ? 64 : m;
+  (void)G;
+  return 64;
 }
 
 int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int32_t requested,

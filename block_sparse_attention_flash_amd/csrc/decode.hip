@@ -12,23 +12,28 @@
 // Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back",
 // 2016), applied to the max operator:
 //
-//   phase 1  stream the split's K blocks, scores q.K^T (G rows x 64 keys per
-//            block) with the 16x16x32 bf16 MFMA, keep all scores of the split
-//            in LDS, block row maxima
+//   phase 1  stream the split's K blocks (each wave its own blocks, the next
+//            block prefetched into registers), scores q.K^T (G rows x 64 keys
+//            per block) with the 16x16x32 bf16 MFMA, block row maxima only
 //   publish  the split aggregate (max over its blocks), look back over earlier
 //            splits for their inclusive prefix, publish the inclusive prefix
 //   phase 2  running max within the split seeded with the exclusive prefix,
 //            tile-wide skip decision per block (strict <, as printed)
-//   phase 3  P = 2^(s - m_ref) for kept blocks, V loads only for kept blocks,
-//            O_partial = P V on the vector ALUs (G <= 8 rows), write the
-//            partial (m_ref, l, O) of the split
+//   phase 3  kept blocks only: reload K (the scores are recomputed, bit for
+//            bit the phase-1 values: same MFMA on the same data) and load V,
+//            P = 2^(s - m_ref), O_partial = P V on the vector ALUs (G <= 8
+//            rows), write the partial (m_ref, l, O) of the split.  Keeping the
+//            scores out of LDS keeps the work-group small, so enough of them
+//            share a CU to keep HBM busy while some sit in phases 2-3.
 //   combine  merge the splits of each (sequence, head): online-softmax
 //            rescaling (attention tutorial section 4.2)
 //
-// Forward progress: split work items are handed out through an atomic ticket
-// in (split, sequence, head) order, so a split only ever waits for splits that
-// already hold a ticket, i.e. are resident or finished.  Every wait is also
-// bounded; a timed-out wait sets the workspace health word instead of hanging.
+// Forward progress: a work-group takes its (sequence, K/V head) from its index
+// and its split number from an atomic ticket of that pair, so a split only
+// ever waits for splits that already hold a ticket, i.e. are resident or
+// finished.  One counter per pair keeps the ticket atomics from serialising on
+// a single address.  Every wait is also bounded; a timed-out wait sets the
+// workspace health word instead of hanging.
 
 #include "device_common.h"
 #include "internal.h"
@@ -38,28 +43,36 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int BC = 64;
-constexpr int kMaxScores = 8192;  // floats of LDS score storage per split
 constexpr int kSpinLimit = 1 << 20;  // ~1 s; a normal wait is well under 1 ms
 
-template <int D, int G>
-struct DecSmem {
-  float score[kMaxScores];      // [G][bps * 64], log2 units
-  float bm[64][G];              // block row maxima
-  float m_ref[G];
-  float lsum[4][G];
-  float pre[G];
-  int kept[64];
-  int nkept;
-  int ticket;
-  float obuf[4][G][D];
-};
+// Look-back words are written and read with device-coherent relaxed atomics
+// (no L2 write-back / invalidate, which an acquire-release pair would cost on
+// every split).  Ordering: the writer waits until its value stores have
+// completed (vmcnt(0)) before it stores the flag, so a reader that sees the
+// flag and then loads the values gets the published ones.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish_flag(int* flag, int v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
 
 // Wait for a look-back flag.  Bounded: gives up after kSpinLimit polls, or at
 // once when another work-group has already given up (health word set).
-__device__ __forceinline__ int spin_acquire(const int* flag, int* health) {
+__device__ __forceinline__ int spin_flag(const int* flag, int* health) {
   for (int n = 0; n < kSpinLimit; ++n) {
-    const int f = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    if (f != 0) return f;
+    const int f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (f != 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return f;
+    }
     if (__hip_atomic_load(health, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return 0;
     __builtin_amdgcn_s_sleep(2);
   }
@@ -67,10 +80,47 @@ __device__ __forceinline__ int spin_acquire(const int* flag, int* health) {
   return 0;
 }
 
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
+template <int D, int G>
+struct DecSmem {
+  float bm[64][G];              // block row maxima (log2 units)
+  float m_ref[G];
+  float lsum[4][G];
+  float pre[G];
+  float pbuf[4][G][64];         // per-wave P of the kept block in flight
+  int kept[64];
+  int nkept;
+  int ticket;
+  float obuf[4][G][D];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k_block(bf16x8 (&kf)[4][D / 32], const __bf16* kbase, int64_t ks_t, int j, int L,
+                                             int r16, int q16) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int key = min(j * BC + 16 * kt + r16, L - 1);  // past L: any valid key, masked below
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      kf[kt][ks] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * ks_t + 32 * ks + 8 * q16);
+  }
 }
+
+// scores (log2 units) of one block: acc[kt][i] = row 4*q16+i, key 16*kt + r16
+template <int D>
+__device__ __forceinline__ void block_scores(f32x4 (&acc)[4], const bf16x8 (&kf)[4][D / 32], const bf16x8 (&qa)[D / 32],
+                                             float c2, int j, int L, int r16) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x4 a = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) a = mfma16(qa[ks], kf[kt][ks], a);
+    const bool ok = j * BC + 16 * kt + r16 < L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[kt][i] = ok ? a[i] * c2 : kNegInf;
+  }
+}
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int D, int G>
 __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, DecodeWorkspace wl) {
@@ -87,25 +137,23 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   float* accw = reinterpret_cast<float*>(ws + wl.acc);
   int* counts = reinterpret_cast<int*>(ws + wl.counts);
 
-  if (tid == 0) sm.ticket = atomicAdd(&header[0], 1);
-  __syncthreads();
   const int S = p.num_splits;
   const int pairs = p.B * p.Hkv;
-  const int ticket = sm.ticket;
-  const int s = ticket / pairs;
-  const int pair = ticket % pairs;
+  const int pair = blockIdx.x % pairs;
+  int* tickets = reinterpret_cast<int*>(ws + wl.tickets);
+  if (tid == 0) sm.ticket = atomicAdd(&tickets[pair], 1);
+  __syncthreads();
+  const int s = sm.ticket;
   const int b = pair / p.Hkv, g = pair % p.Hkv;
   const int unit = pair * S + s;
   const int blk0 = s * p.blocks_per_split;
   const int nb = min(p.blocks_per_split, p.Tc - blk0);
-  const int span = p.blocks_per_split * BC;  // score row pitch
   const float c2 = p.scale * kLog2e;
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
 
-  // ---- phase 1: scores and block maxima --------------------------------------
   // A operand = q rows (row = lane%16 < G, zero otherwise), B operand = K keys.
   const int r16 = lane & 15, q16 = lane >> 4;
   bf16x8 qa[KS];
@@ -116,44 +164,29 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
     else
       qa[ks] = bf16x8{};
   }
-  for (int lb = wave; lb < nb; lb += 4) {
-    const int j = blk0 + lb;
-    bf16x8 kf[4][KS];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = j * BC + 16 * kt + r16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (key < p.L)
-          kf[kt][ks] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * p.ks_t + 32 * ks + 8 * q16);
-        else
-          kf[kt][ks] = bf16x8{};
-      }
-    }
-    float bmax[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 acc = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[ks], kf[kt][ks], acc);
-      const int key = j * BC + 16 * kt + r16;
+
+  // ---- phase 1: block maxima, K streamed with one block of register prefetch
+  if (wave < nb) {
+    bf16x8 kcur[4][KS], knxt[4][KS];
+    load_k_block<D>(kcur, kbase, p.ks_t, blk0 + wave, p.L, r16, q16);
+    for (int lb = wave; lb < nb; lb += 4) {
+      if (lb + 4 < nb) load_k_block<D>(knxt, kbase, p.ks_t, blk0 + lb + 4, p.L, r16, q16);
+      f32x4 acc[4];
+      block_scores<D>(acc, kcur, qa, c2, blk0 + lb, p.L, r16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        float x = fmaxf(fmaxf(acc[0][i], acc[1][i]), fmaxf(acc[2][i], acc[3][i]));
+        x = fmaxf(x, __shfl_xor(x, 1));
+        x = fmaxf(x, __shfl_xor(x, 2));
+        x = fmaxf(x, __shfl_xor(x, 4));
+        x = fmaxf(x, __shfl_xor(x, 8));
         const int row = 4 * q16 + i;
-        const float sc = key < p.L ? acc[i] * c2 : kNegInf;
-        if (row < G) sm.score[row * span + lb * BC + 16 * kt + r16] = sc;
-        bmax[i] = fmaxf(bmax[i], sc);
+        if (r16 == 0 && row < G) sm.bm[lb][row] = x;
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = bmax[i];
-      x = fmaxf(x, __shfl_xor(x, 1));
-      x = fmaxf(x, __shfl_xor(x, 2));
-      x = fmaxf(x, __shfl_xor(x, 4));
-      x = fmaxf(x, __shfl_xor(x, 8));
-      const int row = 4 * q16 + i;
-      if (r16 == 0 && row < G) sm.bm[lb][row] = x;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kcur[kt][ks] = knxt[kt][ks];
     }
   }
   __syncthreads();
@@ -166,27 +199,27 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       float x = kNegInf;
       for (int lb = 0; lb < nb; ++lb) x = fmaxf(x, sm.bm[lb][r]);
       agg[r] = x;
-      aggv[unit * 16 + r] = x;
+      store_coherent(&aggv[unit * 16 + r], x);
     }
-    __hip_atomic_store(&flags[unit], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    publish_flag(&flags[unit], 1);
     float pre[G];
 #pragma unroll
     for (int r = 0; r < G; ++r) pre[r] = kNegInf;
     for (int q = s - 1; q >= 0; --q) {
       const int u = pair * S + q;
-      const int f = spin_acquire(&flags[u], &header[1]);
+      const int f = spin_flag(&flags[u], &header[1]);
       if (f == 0) break;  // timed out: health word set, result invalid
       const float* src = (f == 2) ? inclv : aggv;
 #pragma unroll
-      for (int r = 0; r < G; ++r) pre[r] = fmaxf(pre[r], load_agent(src + u * 16 + r));
+      for (int r = 0; r < G; ++r) pre[r] = fmaxf(pre[r], load_coherent(src + u * 16 + r));
       if (f == 2) break;
     }
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      inclv[unit * 16 + r] = fmaxf(pre[r], agg[r]);
+      store_coherent(&inclv[unit * 16 + r], fmaxf(pre[r], agg[r]));
       sm.pre[r] = pre[r];
     }
-    __hip_atomic_store(&flags[unit], 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    publish_flag(&flags[unit], 2);
   }
   __syncthreads();
 
@@ -233,36 +266,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   __syncthreads();
   const int nkept = sm.nkept;
 
-  // ---- phase 3a: P = 2^(s - m_ref) in place for kept blocks, row sums --------
-  {
-    const int key = tid & 63;
-    float lacc[(G + 3) / 4];
-#pragma unroll
-    for (int x = 0; x < (G + 3) / 4; ++x) lacc[x] = 0.0f;
-    for (int k = 0; k < nkept; ++k) {
-      const int lb = sm.kept[k];
-#pragma unroll
-      for (int x = 0; x < (G + 3) / 4; ++x) {
-        const int r = wave + 4 * x;
-        if (r < G) {
-          float* sp = &sm.score[r * span + lb * BC + key];
-          const float e = fast_exp2(*sp - sm.m_ref[r]);  // 2^-inf = 0 for keys >= L
-          *sp = e;
-          lacc[x] += e;
-        }
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < (G + 3) / 4; ++x) {
-      float v = lacc[x];
-      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      const int r = wave + 4 * x;
-      if (lane == 0 && r < G) sm.lsum[0][r] = v;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 3b: O_partial = P V over kept blocks (vector ALUs) --------------
+  // ---- phase 3: kept blocks, one per wave at a time --------------------------
   constexpr int DCH = D / 8;        // 16-byte chunks per key row
   constexpr int KPS = 64 / DCH;     // keys per load step across the wave
   constexpr int STEPS = BC / KPS;
@@ -272,9 +276,18 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   for (int r = 0; r < G; ++r)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
+  float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // rows 4*q16+i, keys of this lane
+  float mref_l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * q16 + i;
+    mref_l[i] = row < G ? sm.m_ref[row] : 0.0f;
+  }
   for (int k = wave; k < nkept; k += 4) {
     const int lb = sm.kept[k];
     const int j = blk0 + lb;
+    bf16x8 kf[4][KS];
+    load_k_block<D>(kf, kbase, p.ks_t, j, p.L, r16, q16);
     u32x4 vv[STEPS];
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
@@ -282,9 +295,23 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       vv[st] = key < p.L ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.ks_t + 8 * dch)
                          : u32x4{0, 0, 0, 0};
     }
+    f32x4 sc[4];
+    block_scores<D>(sc, kf, qa, c2, j, p.L, r16);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * q16 + i;
+        if (row < G) {
+          const float e = fast_exp2(sc[kt][i] - mref_l[i]);  // 2^-inf = 0 for keys >= L
+          lpart[i] += e;
+          sm.pbuf[wave][row][16 * kt + r16] = e;
+        }
+      }
+    lds_fence();
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-      const int kl = lb * BC + st * KPS + kg;
+      const int kl = st * KPS + kg;
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -293,11 +320,23 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       }
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        const float pr = sm.score[r * span + kl];
+        const float pr = sm.pbuf[wave][r][kl];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pr, vf[e], acc[r][e]);
       }
     }
+    lds_fence();
+  }
+  // row sums: lanes of a 16-lane group hold different keys of the same rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = lpart[i];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    const int row = 4 * q16 + i;
+    if (r16 == 0 && row < G) sm.lsum[wave][row] = x;
   }
   // reduce over the key groups of the wave (lanes sharing dch)
 #pragma unroll
@@ -319,14 +358,19 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   }
   if (tid < G) {
     stats[((int64_t)unit * G + tid) * 2 + 0] = sm.m_ref[tid];
-    stats[((int64_t)unit * G + tid) * 2 + 1] = sm.lsum[0][tid];
+    stats[((int64_t)unit * G + tid) * 2 + 1] = sm.lsum[0][tid] + sm.lsum[1][tid] + sm.lsum[2][tid] + sm.lsum[3][tid];
   }
 }
 
 // Merge the S split partials of one (sequence, query head); write bf16 output
-// and the per-(sequence, K/V head) counters.
+// and the per-(sequence, K/V head) counters.  256 threads: NT/D groups of D
+// threads walk disjoint split subsets, then the groups are summed.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p, DecodeWorkspace wl) {
+__global__ __launch_bounds__(NT) void decode_combine_kernel(const DecodeParams p, DecodeWorkspace wl) {
+  constexpr int NGRP = NT / D;
+  __shared__ float red_m[NT];
+  __shared__ float red_l[NGRP];
+  __shared__ float red_o[NGRP][D];
   const char* ws = static_cast<const char*>(p.workspace);
   const float* stats = reinterpret_cast<const float*>(ws + wl.stats);
   const float* accw = reinterpret_cast<const float*>(ws + wl.acc);
@@ -336,24 +380,42 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p,
   const int g = h / p.G, r = h % p.G;
   const int S = p.num_splits;
   const int pair = b * p.Hkv + g;
-  const int c = threadIdx.x;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, stats[((int64_t)(pair * S + s) * p.G + r) * 2]);
+  const int tid = threadIdx.x, grp = tid / D, c = tid % D;
+  auto ustat = [&](int s) { return ((int64_t)(pair * S + s) * p.G + r); };
+  float m = kNegInf;
+  for (int s = tid; s < S; s += NT) m = fmaxf(m, stats[ustat(s) * 2]);
+  red_m[tid] = m;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if (tid < o) red_m[tid] = fmaxf(red_m[tid], red_m[tid + o]);
+    __syncthreads();
+  }
+  const float M = red_m[0];
   float l = 0.0f, o = 0.0f;
   if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const int64_t u = (int64_t)(pair * S + s) * p.G + r;
-      const float ms = stats[u * 2];
-      if (ms == kNegInf) continue;
-      const float w = fast_exp2(ms - M);
-      l += w * stats[u * 2 + 1];
-      o += w * accw[u * D + c];
+#pragma unroll 4
+    for (int s = grp; s < S; s += NGRP) {
+      const float ms = stats[ustat(s) * 2];
+      const float w = ms == kNegInf ? 0.0f : fast_exp2(ms - M);
+      l += w * stats[ustat(s) * 2 + 1];
+      o += w * accw[ustat(s) * D + c];
     }
   }
-  const float res = l > 0.0f ? o / l : 0.0f;
-  __bf16* out = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)h * p.os_h;
-  out[c] = (__bf16)res;
-  if (p.counters && r == 0 && c == 0) {
+  red_o[grp][c] = o;
+  if (c == 0) red_l[grp] = l;
+  __syncthreads();
+  if (grp == 0) {
+    float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NGRP; ++q) {
+      lt += red_l[q];
+      ot += red_o[q][c];
+    }
+    const float res = lt > 0.0f ? ot / lt : 0.0f;
+    __bf16* out = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)h * p.os_h;
+    out[c] = (__bf16)res;
+  }
+  if (p.counters && r == 0 && tid == 0) {
     int sk = 0;
     for (int s = 0; s < S; ++s) sk += counts[pair * S + s];
     p.counters[2 * pair + 0] = p.Tc;
@@ -361,11 +423,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p,
   }
 }
 
-// Clear the ticket, the health word and the look-back flags (a fill kernel,
+// Clear the health word, the tickets and the look-back flags (a fill kernel,
 // so the sequence stays valid inside captured graphs).
-__global__ void decode_reset_kernel(int* header, int* flags, int n) {
+__global__ void decode_reset_kernel(int* header, int* tickets, int pairs, int* flags, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < 16) header[i] = 0;
+  if (i < pairs) tickets[i] = 0;
   if (i < n) flags[i] = 0;
 }
 
@@ -376,13 +439,14 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const int units = p.B * p.Hkv * p.num_splits;
   const int rb = (units > 16 ? units : 16) + 255;
   hipLaunchKernelGGL(decode_reset_kernel, dim3(rb / 256), dim3(256), 0, s, reinterpret_cast<int*>(ws + wl.header),
-                     reinterpret_cast<int*>(ws + wl.flags), units);
+                     reinterpret_cast<int*>(ws + wl.tickets), p.B * p.Hkv, reinterpret_cast<int*>(ws + wl.flags),
+                     units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.Hq), dim3(D), 0, s, p, wl);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.Hq), dim3(NT), 0, s, p, wl);
   return hipGetLastError();
 }
 
@@ -399,7 +463,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 int launch_decode(const DecodeParams& p, void* stream) {
-  if (p.blocks_per_split * BC * p.G > kMaxScores || p.blocks_per_split > 64) return (int)hipErrorInvalidValue;
+  if (p.blocks_per_split > 64) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return p.d == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
 }
