@@ -131,8 +131,9 @@ def test_decode_split_policy():
     S = bsa.decode_num_splits(32, 32, 8, 131072, 128)
     assert S == 64
     assert bsa.decode_num_splits(1, 4, 1, 4096, 128) >= 2
-    # an explicit count is honoured up to the LDS limit of 32 blocks per split at G = 4
+    # an explicit count is honoured up to 64 blocks per split (one 64-bit skip mask)
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=4) == 4
-    assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=1) == 2
+    assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=1) == 1
+    assert bsa.decode_num_splits(1, 4, 1, 128 * 64, 128, num_splits=1) == 2
     assert bsa.decode_workspace_size(32, 32, 8, 131072, 128) > 32 * 8 * 64 * 4 * 128 * 4
     assert bsa.decode_workspace_size(0, 1, 1, 1, 64) == 0
