@@ -27,9 +27,11 @@
 // P <= 256 (exact in the bf16/fp32 ranges) and removes most O rescales.
 // The skip test always uses the true running max.
 //
-// K/V blocks are staged global -> registers -> LDS, double buffered, with
-// one barrier per block (two when the vote is on).  Two work-groups share a
-// CU, so one group's exponentials overlap the other's MFMAs.
+// K/V blocks stream global -> LDS directly (global_load_lds_dwordx4) into a
+// ring of stages (three at d = 64, two at d = 128), swizzled so that the
+// K-fragment reads and the V transpose reads are bank-conflict free; one
+// barrier per block (two when the vote is on).  Several work-groups share a
+// CU, so one group's exponentials overlap another's MFMAs.
 //
 // Long static tiles can be cut into chunks by a host schedule; a chunk
 // writes its (reference max, row sum, unnormalised O) and a merge kernel
@@ -49,45 +51,79 @@ constexpr int BC = 64;
 constexpr int NT = 256;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 64 x D bf16 tile in LDS as 16-byte chunks, chunk c of row r stored at
+// r*CH + (c ^ xor(r)).  K tiles are read 16 rows x 1 chunk at a time (MFMA A
+// operand), V tiles 4 rows x 4 chunks (transpose reads): each gets its own
+// swizzle so that either access pattern touches 64 distinct banks.
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;
+  __device__ static __forceinline__ int kxor(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int vxor(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __device__ static __forceinline__ int kpos(int r, int c) { return (r * CH + (c ^ kxor(r))) * 8; }
+  __device__ static __forceinline__ int vpos(int r, int c) { return (r * CH + (c ^ vxor(r))) * 8; }
+};
+
+// K/V ring in LDS: two stages (block j+1 streams in while block j is used).
+// A third stage at d = 64 measured slower: the deeper ring costs occupancy
+// that the extra lead time does not repay.  The loop below supports any depth.
+template <int D>
+constexpr int kStages = 2;
+
 template <int D>
 struct Smem {
-  static constexpr int PITCH = D + 8;  // bf16 elements per LDS row (16 B pad against bank conflicts)
-  __bf16 k[2][BC * PITCH];
-  __bf16 v[2][BC * PITCH];
+  __bf16 k[kStages<D>][BC * D];
+  __bf16 v[kStages<D>][BC * D];
   int vote[2][4];
 };
 
-template <int D>
-__device__ __forceinline__ void load_block_regs(u32x4 (&kr)[D / 32], u32x4 (&vr)[D / 32], const __bf16* kbase,
-                                                const __bf16* vbase, int64_t ks_t, int64_t vs_t, int j, int Nk,
-                                                int tid) {
-  // D/8 chunks of 16 B per key row; 64 * D/8 chunks per block; NT threads
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stream one 64-key tile global -> LDS.  Each wave issues CH/4 instructions of
+// 64 lanes x 16 B; lane l of instruction i lands at LDS chunk (4 i + wave) * 64
+// + l and fetches the logical chunk the swizzle assigns to that slot.  The
+// per-lane part of each source address (row in the tile, swizzled chunk) does
+// not depend on the block and is computed once (TileSrc); a block adds only
+// its first key.  Keys past Nk re-read the last key (finite values; they are
+// masked out of S and meet P = 0 in P.V): that clamped form is used only for
+// a block that reaches past Nk.
+template <int D, bool IS_V>
+struct TileSrc {
+  static constexpr int NI = D / 32;  // instructions per wave per tile
+  int row[NI];                       // key row inside the tile
+  int64_t off[NI];                   // element offset of (row, chunk) from the tile's first key
+  __device__ __forceinline__ void init(int64_t stride_t, int wave, int lane) {
+    constexpr int CH = D / 8;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    const int key = j * BC + r;
-    if (key < Nk) {
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * ks_t + c8 * 8);
-      vr[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * vs_t + c8 * 8);
-    } else {
-      kr[i] = u32x4{0, 0, 0, 0};
-      vr[i] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (4 * i + wave) * 64 + lane;
+      const int r = slot / CH, cp = slot % CH;
+      const int c = cp ^ (IS_V ? Tile<D>::vxor(r) : Tile<D>::kxor(r));
+      row[i] = r;
+      off[i] = (int64_t)r * stride_t + c * 8;
     }
   }
-}
-
-template <int D>
-__device__ __forceinline__ void store_block_lds(const u32x4 (&kr)[D / 32], const u32x4 (&vr)[D / 32], __bf16* ks,
-                                                __bf16* vs, int tid) {
-  constexpr int PITCH = Smem<D>::PITCH;
+  __device__ __forceinline__ void issue(__bf16* tile, const __bf16* gbase, int64_t stride_t, int j, int Nk,
+                                        int wave) const {
+    const __bf16* first = gbase + (int64_t)j * BC * stride_t;
+    const bool ragged = j * BC + BC > Nk;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    *reinterpret_cast<u32x4*>(ks + r * PITCH + c8 * 8) = kr[i];
-    *reinterpret_cast<u32x4*>(vs + r * PITCH + c8 * 8) = vr[i];
+    for (int i = 0; i < NI; ++i) {
+      const __bf16* src = first + off[i];
+      if (ragged) {  // clamp the key to Nk - 1
+        const int key = j * BC + row[i];
+        if (key >= Nk) src = gbase + (int64_t)(Nk - 1) * stride_t + (off[i] - (int64_t)row[i] * stride_t);
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + (4 * i + wave) * 64 * 8), 16, 0, 0);
+    }
   }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Work-groups per CU the register budget is cut for: three at d = 64 (at most
@@ -97,7 +133,6 @@ constexpr int kMinBlocksPerCu = D == 64 ? 3 : 2;
 
 template <int D, bool CAUSAL, bool DYN>
 __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(const PrefillParams p) {
-  constexpr int PITCH = Smem<D>::PITCH;
   constexpr int KS = D / 16;  // k-steps of the S MFMA
   constexpr int NTD = D / 32; // 32-wide d tiles of the O MFMA
   __shared__ Smem<D> sm;
@@ -174,39 +209,60 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
   float m_run = kNegInf;   // true running max (raw score units)
   float m_ref = kNegInf;   // reference max used in the exponent (raw units)
-  float l_part = 0.0f;     // this lane's half of the row sum
+  float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's half of the row sum, four partial sums
   f32x16 oacc[NTD];
 #pragma unroll
   for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
   int skipped = 0;
 
-  u32x4 kr[D / 32], vr[D / 32];
-  if (nblk > 0) {
-    const int j0 = cols ? cols[0] : e0;
-    load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, j0, p.Nk, tid);
-    store_block_lds<D>(kr, vr, sm.k[0], sm.v[0], tid);
-  }
+  constexpr int ST = kStages<D>;
+  constexpr int DMA_PER_BLOCK = 2 * (D / 32);  // K and V, CH/4 instructions each per wave
+  auto blk = [&](int i) __attribute__((always_inline)) { return cols ? cols[i] : e0 + i; };
+  TileSrc<D, false> ksrc;
+  TileSrc<D, true> vsrc;
+  ksrc.init(p.ks_t, wave, lane);
+  vsrc.init(p.vs_t, wave, lane);
+  auto fetch = [&](int i) __attribute__((always_inline)) {
+    const int stg = i % ST;
+    const int jj = blk(i);
+    ksrc.issue(sm.k[stg], kbase, p.ks_t, jj, p.Nk, wave);
+    vsrc.issue(sm.v[stg], vbase, p.vs_t, jj, p.Nk, wave);
+  };
+#pragma unroll
+  for (int i = 0; i < ST - 1; ++i)
+    if (i < nblk) fetch(i);
+
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int vr0 = 4 * (g16 >> 1) + (j16 >> 2);
+  const int vcs = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int vhalf = 4 * (j16 & 1);
 
   for (int it = 0; it < nblk; ++it) {
-    const int buf = it & 1;
-    const int j = cols ? cols[it] : e0 + it;
-    __syncthreads();  // block it in LDS; everyone is done with block it-1
-    const bool more = it + 1 < nblk;
-    if (more) {
-      const int jn = cols ? cols[it + 1] : e0 + it + 1;
-      load_block_regs<D>(kr, vr, kbase, vbase, p.ks_t, p.vs_t, jn, p.Nk, tid);
-    }
-    const __bf16* ks = sm.k[buf];
-    const __bf16* vs = sm.v[buf];
+    const int stg = it % ST;
+    const int j = blk(it);
+    // block it has landed once at most the next block's requests are in flight
+    if (ST > 2 && it + 1 < nblk) wait_vmem_le<(ST > 2 ? DMA_PER_BLOCK : 0)>();
+    else wait_vmem_le<0>();
+    __syncthreads();  // block it visible; every wave is done with block it-1's stage
+    if (it + ST - 1 < nblk) fetch(it + ST - 1);
+    const __bf16* ktile = sm.k[stg];
+    const __bf16* vtile = sm.v[stg];
 
-    // ---- S^T = K Q^T : two 32-key tiles
+    // ---- S^T = K Q^T : two 32-key tiles; K-fragment reads run four MFMAs ahead
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    {
+      constexpr int NS = 2 * KS;
+      auto kread = [&](int st) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(ktile + Tile<D>::kpos(32 * (st & 1) + l32, 2 * (st >> 1) + hi));
+      };
+      bf16x8 kfr[4];
 #pragma unroll
-    for (int ks_ = 0; ks_ < KS; ++ks_) {
+      for (int i = 0; i < 4; ++i) kfr[i] = kread(i);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + l32) * PITCH + 16 * ks_ + 8 * hi);
-        sacc[mt] = mfma32(a, qf[ks_], sacc[mt]);
+      for (int st = 0; st < NS; ++st) {
+        sacc[st & 1] = mfma32(kfr[st & 3], qf[st >> 1], sacc[st & 1]);
+        if (st + 4 < NS) kfr[st & 3] = kread(st + 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -237,14 +293,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     if (DYN) {
       const bool agree = (mb == kNegInf) || ((mb - m_new) * c2 < log2_lambda);
       const bool wave_all = __all(agree);
-      if (lane == 0) sm.vote[buf][wave] = wave_all ? 1 : 0;
+      if (lane == 0) sm.vote[it & 1][wave] = wave_all ? 1 : 0;
       __syncthreads();
-      skip = (sm.vote[buf][0] & sm.vote[buf][1] & sm.vote[buf][2] & sm.vote[buf][3]) != 0;
-      if (p.block_state && tid == 0)
-        p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = skip ? 2 : 1;
-    } else if (p.block_state && tid == 0) {
-      p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = 1;
+      const int* vt = sm.vote[it & 1];
+      skip = (vt[0] & vt[1] & vt[2] & vt[3]) != 0;
     }
+    if (p.block_state && tid == 0)
+      p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = skip ? 2 : 1;
     m_run = m_new;
 
     if (!skip) {
@@ -253,14 +308,15 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       if (__any(need)) {
         const float alpha = need ? ((m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c2)) : 1.0f;
         if (need) m_ref = m_new;
-        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l4[i] *= alpha;
 #pragma unroll
         for (int n = 0; n < NTD; ++n)
 #pragma unroll
           for (int a = 0; a < 16; ++a) oacc[n][a] *= alpha;
       }
       const float mref2 = (m_ref == kNegInf) ? 0.0f : m_ref * c2;
-      // ---- P = 2^(S*c2 - m_ref*c2), row sum, pack to bf16 B-operand fragments
+      // ---- P = 2^(S*c2 - m_ref*c2), row sums, pack to bf16 B-operand fragments
       bf16x8 pf[4];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -271,31 +327,27 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
           for (int i = 0; i < 8; ++i) {
             const float e = fast_exp2(fmaf(sacc[mt][8 * hf + i], c2, -mref2));
             pv[i] = e;
-            l_part += e;
+            l4[i & 3] += e;
           }
           pf[2 * mt + hf] = to_bf16x8(pv);
         }
       }
       // ---- O^T += V^T P^T : 4 key steps of 16 x NTD d tiles
-      const int g16 = lane >> 4, j16 = lane & 15;
-      const int vrow = 4 * (g16 >> 1) + (j16 >> 2);
-      const int vcol = 16 * (g16 & 1) + 4 * (j16 & 3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int n = 0; n < NTD; ++n) {
-          const __bf16* src = vs + (16 * kk + vrow) * PITCH + 32 * n + vcol;
-          const i16x4 lo = lds_read_tr16(src);
-          const i16x4 hi4 = lds_read_tr16(src + 8 * PITCH);
+          const int r = 16 * kk + vr0, c = 4 * n + vcs;
+          const i16x4 lo = lds_read_tr16(vtile + Tile<D>::vpos(r, c) + vhalf);
+          const i16x4 hi4 = lds_read_tr16(vtile + Tile<D>::vpos(r + 8, c) + vhalf);
           oacc[n] = mfma32(join_bf16x4(lo, hi4), pf[kk], oacc[n]);
         }
       }
     } else {
       ++skipped;
     }
-
-    if (more) store_block_lds<D>(kr, vr, sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
   }
+  const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
 
   // ---- epilogue: O / l, bf16 store (or the partial of a cut tile)
   const float l_tot = l_part + __shfl_xor(l_part, 32);
