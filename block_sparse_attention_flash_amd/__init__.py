@@ -12,9 +12,11 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``validate_block_index(row_ptr, col_idx, Tc)``
 * ``tile_order_lpt(row_ptr)`` -> int32 numpy launch order
 * ``build_schedule(row_ptr, max_blocks_per_item)`` -> Schedule (host arrays, counts)
-* ``prefill_workspace_size(B, Hq, d, n_slots)``
+* ``prefill_workspace_size(B, Hq, d, n_slots)``, ``prefill_workspace(...)`` (zero-filled)
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
+* ``prefill_plan(...)``, ``decode_plan(...)`` -> Plan: the same calls marshalled
+  once; ``plan(stream=None)`` enqueues with a single C-ABI call
 * ``decode_workspace_size(...)``, ``decode_num_splits(...)``, ``decode_check(workspace)``
 """
 
@@ -30,7 +32,7 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
-    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_fwd", "decode_fwd", "decode_workspace_size", "decode_num_splits", "decode_check",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_num_splits", "decode_check",
 ]
 
 
@@ -158,7 +160,7 @@ def build_schedule(row_ptr, max_blocks_per_item: int) -> Schedule:
     lib = library()
     _check(lib.bsattn_build_schedule(row_ptr.ctypes.data, Tr, int(max_blocks_per_item), None, 0, None, 0,
                                      C.byref(ni), C.byref(nm), C.byref(ns)))
-    items = np.zeros((ni.value, 4), np.int32)
+    items = np.zeros((ni.value, 5), np.int32)
     merges = np.zeros((max(1, nm.value), 3), np.int32)
     _check(lib.bsattn_build_schedule(row_ptr.ctypes.data, Tr, int(max_blocks_per_item), items.ctypes.data,
                                      ni.value, merges.ctypes.data, merges.shape[0], C.byref(ni), C.byref(nm),
@@ -168,6 +170,12 @@ def build_schedule(row_ptr, max_blocks_per_item: int) -> Schedule:
 
 def prefill_workspace_size(B: int, Hq: int, d: int, n_slots: int) -> int:
     return int(library().bsattn_prefill_workspace_size(B, Hq, d, n_slots))
+
+
+def prefill_workspace(B: int, Hq: int, d: int, n_slots: int, device):
+    """A zero-filled prefill workspace (its arrival counters must start at zero;
+    each call leaves them at zero, so the tensor can be reused on one stream)."""
+    return _torch().zeros(prefill_workspace_size(B, Hq, d, n_slots), dtype=_torch().uint8, device=device)
 
 
 # ---------------------------------------------------------------------------
@@ -190,18 +198,26 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
-                Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
-                out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
-                workspace=None, stream=None):
-    """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
+class Plan:
+    """A marshalled call: the C argument struct is built once; each call of the
+    plan enqueues the operation on a stream (default: torch's current stream)
+    with one C-ABI call.  The plan keeps a reference to every tensor it points
+    at; the caller must not resize or reallocate them while the plan is used."""
 
-    ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
-    ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
-    [B, Hq, Tr, Tc] are optional device outputs.  ``schedule`` (from
-    ``build_schedule``, device copies made with ``.to``) cuts long tiles;
-    its partials go to ``workspace`` (uint8 device tensor, allocated here if
-    None).  Returns ``out``."""
+    def __init__(self, fn, args, out, keep):
+        self._fn, self._args, self.out, self._keep = fn, args, out, keep
+        self._ref = C.byref(args)
+
+    def __call__(self, stream=None):
+        _check(self._fn(self._ref, C.c_void_p(_stream_handle(stream))))
+        return self.out
+
+
+def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
+                 Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
+                 out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
+                 workspace=None) -> Plan:
+    """Marshal a prefill (arguments as ``prefill_fwd``) into a reusable Plan."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
         dt = _abi.BSATTN_BF16
@@ -238,12 +254,29 @@ def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, cau
         a.sched_merges, a.n_merges, a.n_slots = _ptr(schedule.d_merges), schedule.n_merges, schedule.n_slots
         if schedule.n_slots > 0:
             if workspace is None:
-                workspace = torch.empty(prefill_workspace_size(B, Hq, d, schedule.n_slots), dtype=torch.uint8,
-                                        device=q.device)
+                workspace = prefill_workspace(B, Hq, d, schedule.n_slots, q.device)
             a.workspace = _ptr(workspace)
             a.workspace_bytes = int(workspace.numel() * workspace.element_size())
-    _check(library().bsattn_prefill_fwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
-    return out
+    keep = (q, k, v, row_ptr, col_idx, tile_order, tile_counters, block_state, schedule, workspace)
+    return Plan(library().bsattn_prefill_fwd, a, out, keep)
+
+
+def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
+                Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
+                out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
+                workspace=None, stream=None):
+    """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
+
+    ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
+    ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
+    [B, Hq, Tr, Tc] are optional device outputs.  ``schedule`` (from
+    ``build_schedule``, device copies made with ``.to``) cuts long tiles;
+    its partials go to ``workspace`` (a uint8 device tensor from
+    ``prefill_workspace``, allocated here if None).  Returns ``out``."""
+    return prefill_plan(q, k, v, scale=scale, lam=lam, causal=causal, Br=Br, Bc=Bc, row_ptr=row_ptr,
+                        col_idx=col_idx, tile_order=tile_order, n_valid=n_valid, out=out,
+                        tile_counters=tile_counters, block_state=block_state, schedule=schedule,
+                        workspace=workspace)(stream)
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:
@@ -254,13 +287,10 @@ def decode_num_splits(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, n
     return int(library().bsattn_decode_num_splits(B, Hq, Hkv, L, d, Bc, num_splits))
 
 
-def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
-               Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
-               stream=None):
-    """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
-
-    ``workspace`` is a uint8 device tensor of at least
-    ``decode_workspace_size`` bytes (allocated here if None)."""
+def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
+                Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None,
+                block_state=None) -> Plan:
+    """Marshal a decode (arguments as ``decode_fwd``) into a reusable Plan."""
     torch = _torch()
     B, Hq, d = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
@@ -287,8 +317,19 @@ def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     a.counters, a.block_state = _ptr(counters), _ptr(block_state)
-    _check(library().bsattn_decode_fwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
-    return out
+    keep = (q, k_cache, v_cache, workspace, counters, block_state)
+    return Plan(library().bsattn_decode_fwd, a, out, keep)
+
+
+def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
+               Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
+               stream=None):
+    """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``decode_workspace_size`` bytes (allocated here if None)."""
+    return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
+                       workspace=workspace, out=out, counters=counters, block_state=block_state)(stream)
 
 
 def decode_check(workspace) -> int:

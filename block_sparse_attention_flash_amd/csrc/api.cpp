@@ -73,6 +73,7 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   w.o = off;   off = align256(off + units * 128 * (size_t)d * sizeof(float));
   w.ml = off;  off = align256(off + units * 128 * 2 * sizeof(float));
   w.cnt = off; off = align256(off + units * 2 * sizeof(int32_t));
+  w.arrive = off; off = align256(off + units * sizeof(int32_t));  // n_merges <= n_slots
   w.total = off;
   return w;
 }
@@ -168,7 +169,8 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
     if (a->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "schedules are implemented for the bf16 path");
     if (!a->row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a schedule needs the CSR (row_ptr, col_idx)");
     if (a->n_items < 1) return fail(BSATTN_ERR_INVALID_ARG, "n_items must be >= 1");
-    if (a->n_slots < 0 || a->n_merges < 0 || (a->n_merges > 0) != (a->n_slots > 0) || (a->n_merges > 0 && !a->sched_merges))
+    if (a->n_slots < 0 || a->n_merges < 0 || (a->n_merges > 0) != (a->n_slots > 0) || (a->n_merges > 0 && !a->sched_merges) ||
+        a->n_merges > a->n_slots)
       return fail(BSATTN_ERR_INVALID_ARG, "inconsistent schedule counts (n_merges, n_slots, sched_merges)");
     if (a->n_slots > 0 && a->lambda > 0.0f)
       return fail(BSATTN_ERR_UNSUPPORTED, "a schedule that cuts tiles needs lambda == 0 (BLASST decisions span the row)");
@@ -182,6 +184,7 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
       p.part_o = reinterpret_cast<float*>(ws + w.o);
       p.part_ml = reinterpret_cast<float*>(ws + w.ml);
       p.part_cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+      p.arrive = reinterpret_cast<int32_t*>(ws + w.arrive);
     }
     p.sched_items = a->sched_items; p.n_items = a->n_items;
     p.sched_merges = a->sched_merges; p.n_merges = a->n_merges; p.n_slots = a->n_slots;

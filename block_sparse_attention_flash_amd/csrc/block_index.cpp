@@ -254,7 +254,7 @@ bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t 
   if (!row_ptr || Tr < 1 || !n_items || !n_merges || !n_slots)
     return fail(BSATTN_ERR_INVALID_ARG, "row_ptr / counts NULL or Tr < 1");
   if (max_blocks < 1) return fail(BSATTN_ERR_INVALID_ARG, "max_blocks_per_item must be >= 1");
-  struct Item { int32_t tile, first, end, slot; };
+  struct Item { int32_t tile, first, end, slot, merge; };
   std::vector<Item> it;
   std::vector<int32_t> mg;
   int32_t slots = 0;
@@ -263,14 +263,15 @@ bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t 
     if (e < b) return fail(BSATTN_ERR_INVALID_ARG, "row_ptr decreases at tile %d", t);
     const int32_t n = e - b;
     if (n <= max_blocks) {
-      it.push_back({t, b, e, -1});
+      it.push_back({t, b, e, -1, -1});
       continue;
     }
     const int32_t k = (n + max_blocks - 1) / max_blocks;  // chunks of near-equal size
+    const int32_t m = (int32_t)(mg.size() / 3);
     mg.insert(mg.end(), {t, slots, k});
     for (int32_t c = 0; c < k; ++c) {
       const int32_t cb = b + (int32_t)((int64_t)n * c / k), ce = b + (int32_t)((int64_t)n * (c + 1) / k);
-      it.push_back({t, cb, ce, slots + c});
+      it.push_back({t, cb, ce, slots + c, m});
     }
     slots += k;
   }
@@ -282,10 +283,12 @@ bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t 
   if (items_capacity < *n_items || (*n_merges > 0 && (!merges || merges_capacity < *n_merges)))
     return fail(BSATTN_ERR_CAPACITY, "schedule needs %d items and %d merges", *n_items, *n_merges);
   for (size_t i = 0; i < it.size(); ++i) {
-    items[4 * i + 0] = it[i].tile;
-    items[4 * i + 1] = it[i].first;
-    items[4 * i + 2] = it[i].end;
-    items[4 * i + 3] = it[i].slot;
+    int32_t* o = items + 5 * i;
+    o[0] = it[i].tile;
+    o[1] = it[i].first;
+    o[2] = it[i].end;
+    o[3] = it[i].slot;
+    o[4] = it[i].merge;
   }
   if (!mg.empty()) std::memcpy(merges, mg.data(), mg.size() * sizeof(int32_t));
   return BSATTN_OK;

@@ -45,23 +45,11 @@ constexpr int NT = 256;
 constexpr int BC = 64;
 constexpr int kSpinLimit = 1 << 20;  // ~1 s; a normal wait is well under 1 ms
 
-// Look-back words are written and read with device-coherent relaxed atomics
-// (no L2 write-back / invalidate, which an acquire-release pair would cost on
-// every split).  Ordering: the writer waits until its value stores have
-// completed (vmcnt(0)) before it stores the flag, so a reader that sees the
-// flag and then loads the values gets the published ones.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// Look-back words are written and read with the device-coherent helpers of
+// device_common.h; the flag is stored only after the value stores completed.
 __device__ __forceinline__ void publish_flag(int* flag, int v) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_stores_done();
   __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Wait for a look-back flag.  Bounded: gives up after kSpinLimit polls, or at

@@ -59,6 +59,32 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Data handed between work-groups of one launch (which may sit on different
+// XCDs, each with its own L2) goes through device-coherent relaxed atomics:
+// no L2 write-back / invalidate, which an acquire-release pair would cost.
+// Protocol: the writer stores its values with store_coherent, waits until
+// they completed (wait_stores_done: on gfx9 vmcnt also counts stores), then
+// signals with an atomic; a reader that has seen the signal reads the values
+// with load_coherent.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
 }  // namespace bsattn

@@ -38,18 +38,20 @@ struct PrefillParams {
   int32_t Tr, Tc;
   int32_t* tile_counters;
   uint8_t* block_state;
-  const int32_t* sched_items;   // [n_items][4] or NULL
+  const int32_t* sched_items;   // [n_items][5] or NULL
   int32_t n_items;
   const int32_t* sched_merges;  // [n_merges][3]
   int32_t n_merges;
   int32_t n_slots;
-  float* part_o;                // [n_slots][B][Hq][128][d]
+  float* part_o;                // [n_slots][B][Hq][128 * d], in accumulator order (see the kernel)
   float* part_ml;               // [n_slots][B][Hq][128][2]  (reference max in raw score units, row sum)
   int32_t* part_cnt;            // [n_slots][B][Hq][2]
+  int32_t* arrive;              // [n_merges][B][Hq] chunk arrival counters (zero between calls)
+  int32_t rank_major;           // bf16 kernel: XCD work order (set by its launcher)
 };
 
 struct PrefillWorkspace {
-  size_t o, ml, cnt, total;
+  size_t o, ml, cnt, arrive, total;
 };
 PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int32_t n_slots);
 

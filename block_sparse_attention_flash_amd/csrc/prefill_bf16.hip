@@ -28,14 +28,15 @@
 // The skip test always uses the true running max.
 //
 // K/V blocks stream global -> LDS directly (global_load_lds_dwordx4) into a
-// ring of stages (three at d = 64, two at d = 128), swizzled so that the
+// two-stage ring, swizzled so that the
 // K-fragment reads and the V transpose reads are bank-conflict free; one
 // barrier per block (two when the vote is on).  Several work-groups share a
 // CU, so one group's exponentials overlap another's MFMAs.
 //
 // Long static tiles can be cut into chunks by a host schedule; a chunk
-// writes its (reference max, row sum, unnormalised O) and a merge kernel
-// combines the chunks (online-softmax rescaling, attention tutorial 4.2).  As in the BLASST notes
+// publishes its (reference max, row sum, unnormalised O) and the last chunk
+// of the tile to finish combines them in slot order (online-softmax
+// rescaling, attention tutorial 4.2), in the same launch.  As in the BLASST notes
 // section 4.1, the prefill still streams V for blocks it skips: prefill is
 // compute bound and the load is issued one block ahead, before the skip
 // decision is known.
@@ -121,6 +122,10 @@ struct TileSrc {
   }
 };
 
+// Partials combined per round trip by the last chunk of a cut tile.
+template <int D>
+constexpr int kMergeBatch = D == 64 ? 3 : 2;
+
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -135,6 +140,7 @@ template <int D, bool CAUSAL, bool DYN>
 __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(const PrefillParams p) {
   constexpr int KS = D / 16;  // k-steps of the S MFMA
   constexpr int NTD = D / 32; // 32-wide d tiles of the O MFMA
+  static_assert(NTD * 16 * NT == BR * D, "one partial = the accumulators of all threads");
   __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
@@ -143,27 +149,47 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: XCD-aware mapping (WG i runs on XCD i % 8), then
-  //      (batch, kv head, tile rank, head in group) with heads innermost so
-  //      the G heads sharing K/V run together on one XCD.
+  // ---- work item.  Work-group i runs on XCD i % 8.  When the (batch, kv
+  //      head) groups divide into 8, group bg lives on XCD bg % 8, so its K/V
+  //      stays in one L2, and the G query heads of a group are adjacent.  An
+  //      XCD takes its work either rank-major (item ranks are longest first,
+  //      so every group's long items start before any short one: the better
+  //      tail when the XCD has few waves of work) or group-major (consecutive
+  //      tiles of one group share K/V blocks in L2: better over many waves).
   const int units = p.sched_items ? p.n_items : p.Tr;
   const int G = p.Hq / p.Hkv;
-  const int64_t W = (int64_t)p.B * p.Hq * units;
-  int64_t wi = blockIdx.x;
-  if ((W & 7) == 0) wi = (wi & 7) * (W >> 3) + (wi >> 3);
-  const int hh = (int)(wi % G);
-  wi /= G;
-  const int rank = (int)(wi % units);
-  wi /= units;
-  const int g = (int)(wi % p.Hkv);
-  const int b = (int)(wi / p.Hkv);
+  const int NBG = p.B * p.Hkv;
+  int hh, rank, bg;
+  if ((NBG & 7) == 0) {
+    const int per = NBG >> 3;
+    int64_t k = blockIdx.x >> 3;
+    hh = (int)(k % G);
+    k /= G;
+    if (p.rank_major) {
+      bg = (int)(k % per) * 8 + (int)(blockIdx.x & 7);
+      rank = (int)(k / per);
+    } else {
+      rank = (int)(k % units);
+      bg = (int)(k / units) * 8 + (int)(blockIdx.x & 7);
+    }
+  } else {
+    int64_t k = blockIdx.x;
+    hh = (int)(k % G);
+    k /= G;
+    bg = (int)(k % NBG);
+    rank = (int)(k / NBG);
+  }
+  const int g = bg % p.Hkv;
+  const int b = bg / p.Hkv;
   const int h = g * G + hh;
-  int t, e0, e1, slot = -1;
+  int t, e0, e1, slot = -1, mrg = -1;
   if (p.sched_items) {
-    t = p.sched_items[4 * rank + 0];
-    e0 = p.sched_items[4 * rank + 1];
-    e1 = p.sched_items[4 * rank + 2];
-    slot = p.sched_items[4 * rank + 3];
+    const int32_t* item = p.sched_items + 5 * rank;
+    t = item[0];
+    e0 = item[1];
+    e1 = item[2];
+    slot = item[3];
+    mrg = item[4];
   } else {
     t = p.tile_order ? p.tile_order[rank] : (CAUSAL ? p.Tr - 1 - rank : rank);
     e0 = p.row_ptr ? p.row_ptr[t] : 0;
@@ -348,118 +374,121 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     }
   }
   const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  float l_tot = l_part + __shfl_xor(l_part, 32);
+  int vis_tot = nblk, skip_tot = skipped;
 
-  // ---- epilogue: O / l, bf16 store (or the partial of a cut tile)
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  if (slot < 0) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (row_ok) {
-      __bf16* obase =
-          static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
+  if (slot >= 0) {
+    // ---- chunk of a cut tile: publish the partial (unnormalised O relative
+    //      to m_ref, plus m_ref and l), then take an arrival ticket; the last
+    //      chunk to arrive combines all partials of the tile and stores O.
+    const int s0 = p.sched_merges[3 * mrg + 1];
+    const int ns = p.sched_merges[3 * mrg + 2];
+    const int lrow = wave * 32 + l32;
+    auto unit = [&](int sl) __attribute__((always_inline)) { return ((int64_t)sl * p.B + b) * p.Hq + h; };
+    // partials are kept in accumulator order, element (16 n + a) of thread
+    // tid at [16 n + a][tid]: each store / load instruction of a wave covers
+    // 256 contiguous bytes
+    {
+      float* po = p.part_o + unit(slot) * BR * D + tid;
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) {
+      for (int n = 0; n < NTD; ++n)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int dcol = 32 * n + 8 * q4 + 4 * hi;
-          f32x4 v4 = {oacc[n][4 * q4 + 0] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
-                      oacc[n][4 * q4 + 3] * inv};
-          *reinterpret_cast<bf16x4*>(obase + dcol) = __builtin_convertvector(v4, bf16x4);
-        }
+        for (int a = 0; a < 16; ++a) store_coherent(po + (16 * n + a) * NT, oacc[n][a]);
+      if (hi == 0) {
+        store_coherent(p.part_ml + (unit(slot) * BR + lrow) * 2 + 0, m_ref);
+        store_coherent(p.part_ml + (unit(slot) * BR + lrow) * 2 + 1, l_tot);
+      }
+      if (tid == 0) {
+        store_coherent(p.part_cnt + unit(slot) * 2 + 0, nblk);
+        store_coherent(p.part_cnt + unit(slot) * 2 + 1, skipped);
       }
     }
-    if (p.tile_counters && tid == 0) {
-      int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
-      tc[0] = nblk;
-      tc[1] = skipped;
-    }
-  } else {
-    // partial of a cut tile: unnormalised O relative to m_ref, plus (m_ref, l)
-    const int64_t unit = ((int64_t)slot * p.B + b) * p.Hq + h;
-    const int lrow = wave * 32 + l32;
-    float* po = p.part_o + (unit * BR + lrow) * D;
+    wait_stores_done();
+    __syncthreads();  // every wave's partial has completed
+    int32_t* arrive = p.arrive + ((int64_t)mrg * p.B + b) * p.Hq + h;
+    if (tid == 0) sm.vote[0][0] = atomicAdd(arrive, 1);
+    __syncthreads();
+    if (sm.vote[0][0] != ns - 1) return;  // a later chunk merges
+    if (tid == 0) store_coherent(arrive, 0);  // leave the counter at zero for the next call
+
+    // ---- merge, in slot order, with the online rescaling rule:
+    //      M' = max(M, m_s), a = 2^((M - M') c2), w = 2^((m_s - M') c2),
+    //      O = a O + w O_s, l = a l + w l_s.  kMergeBatch slots per round
+    //      trip (the own partial is read back like the others).
+    constexpr int NB = kMergeBatch<D>;
+    float M = kNegInf, l = 0.0f;
 #pragma unroll
-    for (int n = 0; n < NTD; ++n)
+    for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
+    for (int base = s0; base < s0 + ns; base += NB) {
+      float ms[NB], ls[NB];
+      f32x16 os[NB][NTD];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int sl = min(base + u, s0 + ns - 1);  // past the end: a valid slot, ignored below
+        const float* ml = p.part_ml + (unit(sl) * BR + lrow) * 2;
+        ms[u] = load_coherent(ml);
+        ls[u] = load_coherent(ml + 1);
+        const float* po = p.part_o + unit(sl) * BR * D + tid;
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) os[u][n][a] = load_coherent(po + (16 * n + a) * NT);
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (base + u >= s0 + ns || ms[u] == kNegInf) continue;
+        const float Mn = fmaxf(M, ms[u]);
+        const float al = M == kNegInf ? 0.0f : fast_exp2((M - Mn) * c2);
+        const float w = fast_exp2((ms[u] - Mn) * c2);
+        M = Mn;
+        l = fmaf(w, ls[u], l * al);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) oacc[n][a] = fmaf(w, os[u][n][a], oacc[n][a] * al);
+      }
+    }
+    l_tot = l;
+    if (p.tile_counters && tid == 0) {
+      vis_tot = skip_tot = 0;
+      for (int sl = s0; sl < s0 + ns; ++sl) {
+        vis_tot += sl == slot ? nblk : load_coherent(p.part_cnt + unit(sl) * 2);
+        skip_tot += sl == slot ? skipped : load_coherent(p.part_cnt + unit(sl) * 2 + 1);
+      }
+    }
+  }
+
+  // ---- epilogue: O / l, bf16 store
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (row_ok) {
+    __bf16* obase =
+        static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v4 = {oacc[n][4 * q4 + 0], oacc[n][4 * q4 + 1], oacc[n][4 * q4 + 2], oacc[n][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(po + 32 * n + 8 * q4 + 4 * hi) = v4;
-      }
-    if (hi == 0) {
-      p.part_ml[(unit * BR + lrow) * 2 + 0] = m_ref;
-      p.part_ml[(unit * BR + lrow) * 2 + 1] = l_tot;
-    }
-    if (tid == 0) {
-      p.part_cnt[unit * 2 + 0] = nblk;
-      p.part_cnt[unit * 2 + 1] = skipped;
-    }
-  }
-}
-
-// Combine the chunk partials of each cut tile: M = max m_s, w_s = 2^((m_s - M) c2),
-// out = sum w_s O_s / sum w_s l_s.  Two threads per query row.
-template <int D>
-__global__ __launch_bounds__(NT) void prefill_merge_kernel(const PrefillParams p) {
-  const int m = blockIdx.x % p.n_merges;
-  const int bh = blockIdx.x / p.n_merges;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int t = p.sched_merges[3 * m + 0];
-  const int s0 = p.sched_merges[3 * m + 1];
-  const int ns = p.sched_merges[3 * m + 2];
-  const int lrow = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int row = t * BR + lrow;
-  const float c2 = p.scale * kLog2e;
-  auto unit = [&](int s) __attribute__((always_inline)) { return ((int64_t)(s0 + s) * p.B + b) * p.Hq + h; };
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(unit(s) * BR + lrow) * 2]);
-  float acc[D / 2];
-#pragma unroll
-  for (int c = 0; c < D / 2; ++c) acc[c] = 0.0f;
-  float l = 0.0f;
-  if (M != kNegInf) {
-    for (int s = 0; s < ns; ++s) {
-      const float ms = p.part_ml[(unit(s) * BR + lrow) * 2];
-      if (ms == kNegInf) continue;
-      const float w = fast_exp2((ms - M) * c2);
-      l += w * p.part_ml[(unit(s) * BR + lrow) * 2 + 1];
-      const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + (unit(s) * BR + lrow) * D + half * (D / 2));
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const f32x4 x = src[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(w, x[e], acc[4 * c + e]);
+        const int dcol = 32 * n + 8 * q4 + 4 * hi;
+        f32x4 v4 = {oacc[n][4 * q4 + 0] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
+                    oacc[n][4 * q4 + 3] * inv};
+        *reinterpret_cast<bf16x4*>(obase + dcol) = __builtin_convertvector(v4, bf16x4);
       }
     }
   }
-  if (row < p.Nq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h +
-                half * (D / 2);
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      f32x4 v4 = {acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv};
-      *reinterpret_cast<bf16x4*>(o + 4 * c) = __builtin_convertvector(v4, bf16x4);
-    }
-  }
-  if (p.tile_counters && threadIdx.x == 0) {
-    int vis = 0, sk = 0;
-    for (int s = 0; s < ns; ++s) {
-      vis += p.part_cnt[unit(s) * 2];
-      sk += p.part_cnt[unit(s) * 2 + 1];
-    }
+  if (p.tile_counters && tid == 0) {
     int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
-    tc[0] = vis;
-    tc[1] = sk;
+    tc[0] = vis_tot;
+    tc[1] = skip_tot;
   }
 }
 
 template <int D, bool CAUSAL, bool DYN>
-hipError_t launch(const PrefillParams& p, hipStream_t s) {
+hipError_t launch(const PrefillParams& p0, hipStream_t s) {
+  PrefillParams p = p0;
   const int64_t units = p.sched_items ? p.n_items : p.Tr;
   const int64_t grid = (int64_t)p.B * p.Hq * units;
+  // rank-major when one XCD (32 CUs) has under four waves of work-groups
+  p.rank_major = grid / 8 < 4 * 32 * kMinBlocksPerCu<D> ? 1 : 0;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, DYN>), dim3((unsigned)grid), dim3(NT), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_merges == 0) return e;
-  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)(p.n_merges * p.B * p.Hq)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

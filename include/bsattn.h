@@ -131,15 +131,18 @@ bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t*
  * Work schedule for a static CSR (same load-imbalance concern): tiles with
  * more than max_blocks_per_item kept blocks are cut into near-equal chunks of
  * consecutive CSR entries, each chunk a separate work-group writing a partial
- * (running max, row sum, unnormalised output) to the prefill workspace; a
- * merge step then combines the chunks of each cut tile with the online-
- * softmax rescaling rule (attention tutorial section 4.2).  Exact for lambda
- * = 0; a schedule that cuts tiles is refused for lambda > 0, whose skip
- * decisions depend on the whole row (BLASST notes Algorithm 1).
- *   items  [n_items][4]  {tile, first CSR entry, end CSR entry, slot}; slot = -1
- *                        means the item writes the output directly; items are
+ * (running max, row sum, unnormalised output) to the prefill workspace; the
+ * last chunk of a cut tile to finish combines the partials with the online-
+ * softmax rescaling rule (attention tutorial section 4.2), in slot order, and
+ * writes the output.  Exact for lambda = 0; a schedule that cuts tiles is
+ * refused for lambda > 0, whose skip decisions depend on the whole row
+ * (BLASST notes Algorithm 1).
+ *   items  [n_items][5]  {tile, first CSR entry, end CSR entry, slot, merge};
+ *                        slot = merge = -1 means the item writes the output
+ *                        directly, else merge indexes `merges`; items are
  *                        ordered longest first
- *   merges [n_merges][3] {tile, first slot, number of slots}
+ *   merges [n_merges][3] {tile, first slot, number of slots}; the slots of a
+ *                        cut tile are consecutive
  * Two-call pattern: items == NULL returns the counts only.  Host buffers.
  * max_blocks_per_item >= 1.  Returns BSATTN_ERR_CAPACITY if a buffer is short.
  */
@@ -182,7 +185,11 @@ typedef struct {
   int32_t n_merges;
   int32_t n_slots;             /* partial slots of the schedule; > 0 requires lambda == 0 */
   void* workspace;             /* device, >= bsattn_prefill_workspace_size(B, Hq, d, n_slots) bytes,
-                                  256-byte aligned; unused when n_slots == 0 */
+                                  256-byte aligned; unused when n_slots == 0.  Holds the
+                                  partials and one arrival counter per (merge, batch, head):
+                                  zero-fill it once before its first use; every call leaves
+                                  the counters at zero again.  Calls that share a workspace
+                                  must not overlap (same stream, or ordered by events). */
   size_t workspace_bytes;
 } bsattn_prefill_args;
 

@@ -127,13 +127,18 @@ def test_schedule_covers_every_entry_once():
         seen = np.zeros(rp[-1], np.int32)
         tiles_direct = set()
         lens = []
-        for t, a, b, slot in sc.items:
+        assert sc.items.shape[1] == 5
+        for t, a, b, slot, m in sc.items:
             assert rp[t] <= a <= b <= rp[t + 1]
             assert b - a <= mx
             seen[a:b] += 1
             lens.append(b - a)
+            assert (slot < 0) == (m < 0)
             if slot < 0:
                 tiles_direct.add(int(t))
+            else:                                                  # the item's merge owns its slot
+                mt, s0, n = sc.merges[m]
+                assert mt == t and s0 <= slot < s0 + n
         assert (seen == 1).all()
         assert lens == sorted(lens, reverse=True)                  # longest first
         cut = {int(t) for t, s0, n in sc.merges}
@@ -141,7 +146,7 @@ def test_schedule_covers_every_entry_once():
         slots = sorted(int(s) for s in sc.items[:, 3] if s >= 0)
         assert slots == list(range(sc.n_slots))
         for t, s0, n in sc.merges:                                 # slots of a cut tile are consecutive
-            assert sorted(int(s) for tt, a, b, s in sc.items if tt == t) == list(range(s0, s0 + n))
+            assert sorted(int(s) for tt, a, b, s, m in sc.items if tt == t) == list(range(s0, s0 + n))
     assert bsa.build_schedule(rp, 5000).n_slots == 0
 
 
@@ -167,4 +172,6 @@ def test_schedule_validation():
     assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_CAPACITY
     a.n_merges = 0
     assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG   # inconsistent counts
-    assert bsa.prefill_workspace_size(2, 16, 64, 3) >= 3 * 2 * 16 * 128 * 66 * 4
+    assert bsa.prefill_workspace_size(2, 16, 64, 3) >= 3 * 2 * 16 * (128 * 66 * 4 + 3 * 4)
+    a.n_merges, a.n_slots = 4, 2                                   # more merges than slots
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG

@@ -114,3 +114,28 @@ def test_decode_deterministic():
     a = run_decode(cfg, q, kc, vc)
     b = run_decode(cfg, q, kc, vc)
     assert torch.equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+def test_decode_plan_and_graph_replays():
+    """A plan gives the eager result; a HIP graph of it (reset + split + combine
+    kernels) replays bit-identically, with other GPU work between replays."""
+    cfg = DecodeWorkload(name="s", description="", B=2, Hq=8, Hkv=2, L=9000, d=128, Bc=64, lam=40 / 9000, seed=29)
+    _say("decode plan + graph")
+    q, kc, vc = (x.to(DEV) for x in gen_decode_inputs(cfg))
+    ref = bsa.decode_fwd(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=cfg.lam)
+    ws = torch.empty(bsa.decode_workspace_size(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d), dtype=torch.uint8, device=DEV)
+    plan = bsa.decode_plan(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=cfg.lam, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(plan(), ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    for r in range(3):
+        plan.out.fill_(7.0)
+        junk = torch.randn(1 << 20, device=DEV).sum()   # unrelated work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, ref), r
+        assert bsa.decode_check(ws) == 0
+    del junk

@@ -22,7 +22,7 @@ def _say(msg):
     print(f"[gpu-prefill] {msg}", file=sys.stderr, flush=True)
 
 
-def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedule=None):
+def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedule=None, workspace=None):
     """Launch through the binding; returns host copies of out, block_state, counters."""
     Br = cfg.Br if Br is None else Br
     B, N, Hq, d = q.shape
@@ -37,7 +37,7 @@ def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedu
         od = torch.from_numpy(order).to(DEV)
     out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam if lam is None else lam, causal=cfg.causal,
                           Br=Br, Bc=cfg.Bc, row_ptr=rp, col_idx=ci, tile_order=od, n_valid=cfg.n_valid,
-                          tile_counters=counters, block_state=state, schedule=schedule)
+                          tile_counters=counters, block_state=state, schedule=schedule, workspace=workspace)
     torch.cuda.synchronize()
     return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
 
@@ -232,7 +232,15 @@ def test_schedule_cut_tiles_small(max_blocks):
         csr = bsa.build_block_index(spec, n, n, 128, 64)
         sched = bsa.build_schedule(csr[0], max_blocks)
         assert (sched.n_slots > 0) == (int(np.diff(csr[0]).max()) > max_blocks)
-        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched)
+        ws = bsa.prefill_workspace(cfg.B, cfg.Hq, d, max(sched.n_slots, 1), DEV)
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched, workspace=ws)
+        if sched.n_slots:
+            # the arrival counters were left at zero: a second call on the same
+            # workspace merges again, in slot order whichever chunk ends last
+            assert bool((ws != 0).any())  # partials written
+            out2, st2, cnt2 = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched,
+                                          workspace=ws)
+            assert torch.equal(out, out2) and np.array_equal(cnt, cnt2) and np.array_equal(st, st2)
         for b in range(cfg.B):
             for h in range(cfg.Hq):
                 for t in range(3):
@@ -255,3 +263,33 @@ def test_cfg3_full_size_schedule():
             check_prefill_tile(qh, kh, vh, out, st, cnt, 0, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
                                lam=0.0, n_valid=cfg.mask.n_valid, row_ptr=csr[0], col_idx=csr[1], method="two_pass",
                                rows_limit=cfg.mask.n_valid)
+
+
+def test_prefill_plan_and_graph_replays():
+    """A plan gives the eager result; a HIP graph of a cut-tile schedule (whose
+    arrival counters must return to zero) replays bit-identically, with other
+    GPU work between replays."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13
+    cfg = _small("graph", N=n, d=64, Hq=4, Hkv=4, mask=spec, generator="iid_offset")
+    _say("prefill plan + graph, schedule with cut tiles")
+    q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+    rp_h, ci_h = bsa.build_block_index(spec, n, n, 128, 64)
+    sched = bsa.build_schedule(rp_h, 3).to(DEV)
+    assert sched.n_merges > 0
+    rp, ci = torch.from_numpy(rp_h).to(DEV), torch.from_numpy(ci_h).to(DEV)
+    kw = dict(scale=cfg.scale, row_ptr=rp, col_idx=ci, n_valid=spec.n_valid, schedule=sched)
+    ref = bsa.prefill_fwd(q, k, v, **kw)
+    plan = bsa.prefill_plan(q, k, v, **kw)
+    assert torch.equal(plan(), ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    for r in range(3):
+        plan.out.fill_(3.0)
+        junk = torch.randn(1 << 20, device=DEV).sum()   # unrelated work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, ref), r
+    del junk
