@@ -93,8 +93,9 @@ int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int3
     bps = (Tc + S - 1) / S;
   } else {
     // aim for at least ~2048 split work-groups (8 per CU on 256 CUs), splits of 2..cap blocks
+    // (longer splits stream K longer between the latency-bound look-back and V phases)
     int64_t want = ((int64_t)Tc * B * Hkv + 2047) / 2048;
-    bps = (int32_t)(want < 2 ? 2 : (want > 32 ? 32 : want));
+    bps = (int32_t)(want < 2 ? 2 : (want > cap ? cap : want));
   }
   if (bps > cap) bps = cap;
   if (bps < 1) bps = 1;

@@ -126,8 +126,10 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   int* counts = reinterpret_cast<int*>(ws + wl.counts);
 
   const int S = p.num_splits;
-  const int pairs = p.B * p.Hkv;
-  const int pair = blockIdx.x % pairs;
+  // pair-major: the S work-groups of one (sequence, K/V head) are consecutive,
+  // so a pair's last splits (where recent keys usually keep blocks, making
+  // phase 3 long) finish while later pairs still stream K, not all at the end
+  const int pair = blockIdx.x / S;
   int* tickets = reinterpret_cast<int*>(ws + wl.tickets);
   if (tid == 0) sm.ticket = atomicAdd(&tickets[pair], 1);
   __syncthreads();

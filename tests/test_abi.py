@@ -127,13 +127,14 @@ def test_decode_rejects(name, mutate, status):
 
 
 def test_decode_split_policy():
-    # automatic: splits of at most 32 blocks, enough work-groups for the chip
+    # automatic: splits of at most 64 blocks, enough work-groups for the chip
     S = bsa.decode_num_splits(32, 32, 8, 131072, 128)
-    assert S == 64
+    assert S == 32
+    assert bsa.decode_num_splits(1, 32, 8, 131072, 128) == 256      # 8 blocks per split: 2048 work-groups
     assert bsa.decode_num_splits(1, 4, 1, 4096, 128) >= 2
     # an explicit count is honoured up to 64 blocks per split (one 64-bit skip mask)
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=4) == 4
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=1) == 1
     assert bsa.decode_num_splits(1, 4, 1, 128 * 64, 128, num_splits=1) == 2
-    assert bsa.decode_workspace_size(32, 32, 8, 131072, 128) > 32 * 8 * 64 * 4 * 128 * 4
+    assert bsa.decode_workspace_size(32, 32, 8, 131072, 128) > 32 * 8 * 32 * 4 * 128 * 4   # partial O of every split
     assert bsa.decode_workspace_size(0, 1, 1, 1, 64) == 0
