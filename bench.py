@@ -6,8 +6,8 @@
 One step = one pass of the attention hot path over one batch of the named
 synthetic workload, inputs resident in HBM: the prefill kernel for a prefill
 workload (the static block index and schedule are built once, on the host,
-before timing: a fixed mask is not rebuilt per step), or the decode reset,
-split and combine kernels for the decode workload.  Each step is one C-ABI
+before timing: a fixed mask is not rebuilt per step), or the decode kernel
+(splits and their merge) for the decode workload.  Each step is one C-ABI
 call of a prepared plan.
 
 Timing (HIP events on the launch stream): ``ms_per_step`` and ``value`` come
@@ -203,8 +203,7 @@ def run_decode_workload(name: str, steps: int, warmup: int):
     log(f"{name}: generating inputs ({cfg.description})")
     q, kc, vc = gen_decode_inputs(cfg, device=dev)
     Tc = -(-cfg.L // cfg.Bc)
-    ws = torch.empty(bsa.decode_workspace_size(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.Bc), dtype=torch.uint8,
-                     device=dev)
+    ws = bsa.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, dev, cfg.Bc)
     out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.bfloat16, device=dev)
     counters = torch.zeros((cfg.B, cfg.Hkv, 2), dtype=torch.int32, device=dev)
 
@@ -235,7 +234,7 @@ def run_decode_workload(name: str, steps: int, warmup: int):
         "health": health,
         "config": {"workload": f"{name}: {cfg.description}", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "L": cfg.L, "d": cfg.d,
                    "Bc": cfg.Bc, "lambda": cfg.lam, "dtype": "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (+ reset and combine in the timed call)",
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
                      "achieved": gbs_launch, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs_launch / PEAK_HBM_GBS,
                      "per_launch_bytes": algo,
                      "traffic": traffic_for("decode_split_kernel", name)},

@@ -17,7 +17,8 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
 * ``prefill_plan(...)``, ``decode_plan(...)`` -> Plan: the same calls marshalled
   once; ``plan(stream=None)`` enqueues with a single C-ABI call
-* ``decode_workspace_size(...)``, ``decode_num_splits(...)``, ``decode_check(workspace)``
+* ``decode_workspace_size(...)``, ``decode_workspace(...)`` (zero-filled), ``decode_num_splits(...)``,
+  ``decode_check(workspace)`` (reads and clears the health word)
 """
 
 from __future__ import annotations
@@ -32,7 +33,7 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
-    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_num_splits", "decode_check",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits", "decode_check",
 ]
 
 
@@ -283,6 +284,13 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 6
     return int(library().bsattn_decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits))
 
 
+def decode_workspace(B: int, Hq: int, Hkv: int, L: int, d: int, device, Bc: int = 64, num_splits: int = 0):
+    """A zero-filled decode workspace (tickets, flags and counters must start at
+    zero; each call leaves them at zero, so the tensor can be reused on one stream)."""
+    torch = _torch()
+    return torch.zeros(decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits), dtype=torch.uint8, device=device)
+
+
 def decode_num_splits(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:
     return int(library().bsattn_decode_num_splits(B, Hq, Hkv, L, d, Bc, num_splits))
 
@@ -301,9 +309,8 @@ def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional
         raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "head dim must be contiguous")
     if out is None:
         out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
-    need = decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, Hq, Hkv, L, d, q.device, Bc, num_splits)
     a = _abi.DecodeArgs()
     a.q, a.k_cache, a.v_cache, a.out = _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out)
     a.B, a.Hq, a.Hkv, a.L, a.Lmax, a.d = B, Hq, Hkv, L, Lmax, d
@@ -327,7 +334,7 @@ def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[
     """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
 
     ``workspace`` is a uint8 device tensor of at least
-    ``decode_workspace_size`` bytes (allocated here if None)."""
+    ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None)."""
     return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
                        workspace=workspace, out=out, counters=counters, block_state=block_state)(stream)
 

@@ -258,13 +258,18 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   return hip_status(launch_decode(p, stream), "decode launch");
 }
 
-bsattn_status bsattn_decode_check(const void* workspace, int32_t* health_out) {
+bsattn_status bsattn_decode_check(void* workspace, int32_t* health_out) {
   clear_error();
   if (!workspace || !health_out) return fail(BSATTN_ERR_INVALID_ARG, "workspace and health_out must be non-NULL");
   int32_t h = 0;
-  hipError_t e = hipMemcpy(&h, static_cast<const char*>(workspace) + sizeof(int32_t), sizeof(int32_t),
-                           hipMemcpyDeviceToHost);
+  char* word = static_cast<char*>(workspace) + sizeof(int32_t);
+  hipError_t e = hipMemcpy(&h, word, sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  if (h != 0) {
+    const int32_t zero = 0;
+    e = hipMemcpy(word, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  }
   *health_out = h;
   return BSATTN_OK;
 }

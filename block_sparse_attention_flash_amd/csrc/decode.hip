@@ -26,7 +26,9 @@
 //            scores out of LDS keeps the work-group small, so enough of them
 //            share a CU to keep HBM busy while some sit in phases 2-3.
 //   combine  merge the splits of each (sequence, head): online-softmax
-//            rescaling (attention tutorial section 4.2)
+//            rescaling (attention tutorial section 4.2); it also clears the
+//            pair's ticket and look-back flags, so the workspace needs no
+//            clearing between calls (only a zero fill before its first use)
 //
 // Forward progress: a work-group takes its (sequence, K/V head) from its index
 // and its split number from an atomic ticket of that pair, so a split only
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(const DecodeParams p
   __shared__ float red_m[NT];
   __shared__ float red_l[NGRP];
   __shared__ float red_o[NGRP][D];
-  const char* ws = static_cast<const char*>(p.workspace);
+  char* ws = static_cast<char*>(p.workspace);
   const float* stats = reinterpret_cast<const float*>(ws + wl.stats);
   const float* accw = reinterpret_cast<const float*>(ws + wl.acc);
   const int* counts = reinterpret_cast<const int*>(ws + wl.counts);
@@ -411,30 +413,20 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(const DecodeParams p
     p.counters[2 * pair + 0] = p.Tc;
     p.counters[2 * pair + 1] = sk;
   }
-}
-
-// Clear the health word, the tickets and the look-back flags (a fill kernel,
-// so the sequence stays valid inside captured graphs).
-__global__ void decode_reset_kernel(int* header, int* tickets, int pairs, int* flags, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < 16) header[i] = 0;
-  if (i < pairs) tickets[i] = 0;
-  if (i < n) flags[i] = 0;
+  if (r == 0) {  // every split of the pair has finished: clear its ticket and flags
+    int* tickets = reinterpret_cast<int*>(ws + wl.tickets);
+    int* flags = reinterpret_cast<int*>(ws + wl.flags);
+    for (int s = tid; s < S; s += NT) flags[pair * S + s] = 0;
+    if (tid == 0) tickets[pair] = 0;
+  }
 }
 
 template <int D, int G>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const DecodeWorkspace wl = decode_workspace_layout(p.B, p.Hq, p.Hkv, p.d, p.num_splits);
-  char* ws = static_cast<char*>(p.workspace);
   const int units = p.B * p.Hkv * p.num_splits;
-  const int rb = (units > 16 ? units : 16) + 255;
-  hipLaunchKernelGGL(decode_reset_kernel, dim3(rb / 256), dim3(256), 0, s, reinterpret_cast<int*>(ws + wl.header),
-                     reinterpret_cast<int*>(ws + wl.tickets), p.B * p.Hkv, reinterpret_cast<int*>(ws + wl.flags),
-                     units);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.Hq), dim3(NT), 0, s, p, wl);
   return hipGetLastError();

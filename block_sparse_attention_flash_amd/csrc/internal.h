@@ -77,7 +77,7 @@ struct DecodeParams {
 
 // Decode workspace layout (all offsets 256-byte aligned), see decode.hip.
 struct DecodeWorkspace {
-  size_t header;    // [1]: health word
+  size_t header;    // [1]: health word (sticky until bsattn_decode_check reads it)
   size_t tickets;   // int32 [B*Hkv]: split tickets per (sequence, kv head)
   size_t flags;     // int32 [B*Hkv*S]
   size_t agg;       // float [B*Hkv*S*16]  split aggregate max per row

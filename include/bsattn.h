@@ -224,7 +224,10 @@ typedef struct {
   int32_t Bc;             /* 64 */
   int32_t num_splits;     /* splits per (sequence, K/V head); 0 = automatic.  Never changes results
                              beyond float rounding order; never changes the skip set */
-  void* workspace;        /* device, >= bsattn_decode_workspace_size(...) bytes, 256-byte aligned */
+  void* workspace;        /* device, >= bsattn_decode_workspace_size(...) bytes, 256-byte aligned.
+                             Tickets, flags and counters: zero-fill it once before its first use;
+                             every call leaves them at zero again.  Calls that share a workspace
+                             must not overlap (same stream, or ordered by events). */
   size_t workspace_bytes;
   int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks */
   uint8_t* block_state;   /* optional device [B, Hkv, Tc]: 1 computed, 2 skipped */
@@ -238,13 +241,15 @@ size_t bsattn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
 int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
                                  int32_t Bc, int32_t num_splits);
 
-/* Enqueue the decode (split kernel, then the combine kernel) on `stream`. */
+/* Enqueue the decode on `stream`: the split kernel, then the combine kernel
+ * (merge of the splits, attention tutorial section 4.2). */
 bsattn_status bsattn_decode_fwd(const bsattn_decode_args* args, void* stream);
 
-/* Read back the decode workspace health word after the stream has finished
- * (host call, synchronous copy): 0 = fine, else a kernel-side wait timed out
- * and the output of that call is not valid. */
-bsattn_status bsattn_decode_check(const void* workspace, int32_t* health_out);
+/* Read and clear the decode workspace health word after the stream has
+ * finished (host call, synchronous copies): 0 = fine, else a kernel-side wait
+ * timed out in a call since the previous check, and that call's output is not
+ * valid. */
+bsattn_status bsattn_decode_check(void* workspace, int32_t* health_out);
 
 #ifdef __cplusplus
 }

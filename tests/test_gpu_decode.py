@@ -21,12 +21,24 @@ def _say(msg):
     print(f"[gpu-decode] {msg}", file=sys.stderr, flush=True)
 
 
+_WS = [None]
+
+
+def _shared_workspace(nbytes):
+    """One zero-filled workspace reused by every decode call of this module, with
+    different shapes and split counts: each call must leave its tickets, flags
+    and counters at zero for the next."""
+    if _WS[0] is None or _WS[0].numel() < nbytes:
+        _WS[0] = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=DEV)
+    return _WS[0]
+
+
 def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None):
     B, Hq, d = q.shape
     Hkv = kc.shape[2]
     L = kc.shape[1] if L is None else L
     Tc = -(-L // 64)
-    ws = torch.empty(bsa.decode_workspace_size(B, Hq, Hkv, L, d, 64, num_splits), dtype=torch.uint8, device=DEV)
+    ws = _shared_workspace(bsa.decode_workspace_size(B, Hq, Hkv, L, d, 64, num_splits))
     state = torch.zeros((B, Hkv, Tc), dtype=torch.uint8, device=DEV)
     counters = torch.full((B, Hkv, 2), -1, dtype=torch.int32, device=DEV)
     out = bsa.decode_fwd(q, kc, vc, L=L, scale=cfg.scale, lam=cfg.lam if lam is None else lam,
@@ -123,7 +135,7 @@ def test_decode_plan_and_graph_replays():
     _say("decode plan + graph")
     q, kc, vc = (x.to(DEV) for x in gen_decode_inputs(cfg))
     ref = bsa.decode_fwd(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=cfg.lam)
-    ws = torch.empty(bsa.decode_workspace_size(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d), dtype=torch.uint8, device=DEV)
+    ws = bsa.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, DEV)
     plan = bsa.decode_plan(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=cfg.lam, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(plan(), ref)
