@@ -152,6 +152,12 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   if (a->dtype == BSATTN_BF16 && a->Br != 128) return fail(BSATTN_ERR_UNSUPPORTED, "bf16 path needs Br = 128");
   if (a->dtype == BSATTN_FP32 && a->Br != 64 && a->Br != 128)
     return fail(BSATTN_ERR_UNSUPPORTED, "fp32 path needs Br in {64, 128}");
+  if (a->dtype == BSATTN_BF16) {
+    // the bf16 kernel addresses one head's K/V rows with 32-bit byte offsets
+    const int64_t lim = 0xffffffffLL;
+    if (((int64_t)a->Nk + 64) * a->k_stride[1] * 2 > lim || ((int64_t)a->Nk + 64) * a->v_stride[1] * 2 > lim)
+      return fail(BSATTN_ERR_UNSUPPORTED, "bf16 path: (Nk + 64) * token stride must stay below 4 GiB per head");
+  }
   PrefillParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
   p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Nk = a->Nk; p.d = a->d;

@@ -85,6 +85,12 @@ __device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
 
 __device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// max(x of lane l, x of lane l ^ 32) in registers: v_permlane32_swap with the
+// same value in both operands returns, in every lane l, x of lane l % 32
+// (first result) and x of lane l % 32 + 32 (second).  (Checked on the device.)
+__device__ __forceinline__ float wave_max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 }  // namespace bsattn

@@ -27,11 +27,13 @@
 // P <= 256 (exact in the bf16/fp32 ranges) and removes most O rescales.
 // The skip test always uses the true running max.
 //
-// K/V blocks stream global -> LDS directly (global_load_lds_dwordx4) into a
-// two-stage ring, swizzled so that the
-// K-fragment reads and the V transpose reads are bank-conflict free; one
-// barrier per block (two when the vote is on).  Several work-groups share a
-// CU, so one group's exponentials overlap another's MFMAs.
+// K/V blocks stream global -> LDS directly (buffer_load_dwordx4 ... lds,
+// range-checked at the last key) into a two-stage ring, swizzled so that the
+// K-fragment reads and the V transpose reads are bank-conflict free; block
+// j+1 streams in during all of block j's work, and its block index is read
+// two blocks ahead.  One barrier per block (two when the vote is on).
+// Several work-groups share a CU, so one group's exponentials overlap
+// another's MFMAs.
 //
 // Long static tiles can be cut into chunks by a host schedule; a chunk
 // publishes its (reference max, row sum, unnormalised O) and the last chunk
@@ -82,45 +84,85 @@ struct Smem {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Stream one 64-key tile global -> LDS.  Each wave issues CH/4 instructions of
-// 64 lanes x 16 B; lane l of instruction i lands at LDS chunk (4 i + wave) * 64
-// + l and fetches the logical chunk the swizzle assigns to that slot.  The
-// per-lane part of each source address (row in the tile, swizzled chunk) does
-// not depend on the block and is computed once (TileSrc); a block adds only
-// its first key.  Keys past Nk re-read the last key (finite values; they are
-// masked out of S and meet P = 0 in P.V): that clamped form is used only for
-// a block that reaches past Nk.
+// Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle; range checking against num_records).
+constexpr int kBufferWord3 = 0x00020000;
+
+// Global -> LDS loads of one 64-key tile (K or V) through a buffer
+// descriptor whose range ends at the last key: rows of keys >= Nk read as
+// zeros (hardware range check), which the score mask and P = 0 make
+// harmless.  Lane (wave, lane) of instruction i moves one 16-byte chunk; its
+// byte offset inside a tile is fixed, the tile's start is a scalar offset.
 template <int D, bool IS_V>
 struct TileSrc {
   static constexpr int NI = D / 32;  // instructions per wave per tile
-  int row[NI];                       // key row inside the tile
-  int64_t off[NI];                   // element offset of (row, chunk) from the tile's first key
-  __device__ __forceinline__ void init(int64_t stride_t, int wave, int lane) {
+  uint32_t voff[NI];                 // byte offset of (row, chunk) from the tile's first key
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ void init(const __bf16* head, int64_t stride_t, int Nk, int wave, int lane) {
     constexpr int CH = D / 8;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int slot = (4 * i + wave) * 64 + lane;
       const int r = slot / CH, cp = slot % CH;
       const int c = cp ^ (IS_V ? Tile<D>::vxor(r) : Tile<D>::kxor(r));
-      row[i] = r;
-      off[i] = (int64_t)r * stride_t + c * 8;
+      voff[i] = (uint32_t)(((int64_t)r * stride_t + c * 8) * 2);
     }
+    const uint32_t extent = (uint32_t)(((int64_t)(Nk - 1) * stride_t + D) * 2);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, (int)extent, kBufferWord3);
   }
-  __device__ __forceinline__ void issue(__bf16* tile, const __bf16* gbase, int64_t stride_t, int j, int Nk,
-                                        int wave) const {
-    const __bf16* first = gbase + (int64_t)j * BC * stride_t;
-    const bool ragged = j * BC + BC > Nk;
+  __device__ __forceinline__ void issue(__bf16* tile, int64_t stride_t, int j, int wave) const {
+    const uint32_t soff = (uint32_t)((int64_t)j * BC * stride_t * 2);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const __bf16* src = first + off[i];
-      if (ragged) {  // clamp the key to Nk - 1
-        const int key = j * BC + row[i];
-        if (key >= Nk) src = gbase + (int64_t)(Nk - 1) * stride_t + (off[i] - (int64_t)row[i] * stride_t);
-      }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + (4 * i + wave) * 64 * 8), 16, 0, 0);
-    }
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (4 * i + wave) * 64 * 8), 16, voff[i], soff,
+                                               0, 0);
   }
 };
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(ptr);
+}
+
+// The V fragments of one 16-key step of O^T += V^T P^T: for each of the NTD
+// 32-wide d tiles, two ds_read_b64_tr_b16 (keys r and r + 8), issued together
+// and waited for inside the same asm block.  base[n] is this lane's byte
+// address for d tile n at key step 0; step kk adds 32 kk D bytes, the upper
+// 8 keys 16 D bytes.  (The intrinsic form makes the compiler wait for every
+// pending global->LDS load first: it cannot tell the V stage from the stage
+// being filled.)
+template <int D, int KK>
+__device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t (&base)[D / 32]) {
+  constexpr int O0 = 32 * KK * D, O1 = 32 * KK * D + 16 * D;
+  i16x4 x[2 * (D / 32)];
+  if constexpr (D == 64) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%c6\n"
+        "ds_read_b64_tr_b16 %1, %4 offset:%c7\n"
+        "ds_read_b64_tr_b16 %2, %5 offset:%c6\n"
+        "ds_read_b64_tr_b16 %3, %5 offset:%c7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3])
+        : "v"(base[0]), "v"(base[1]), "i"(O0), "i"(O1)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%c12\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:%c13\n"
+        "ds_read_b64_tr_b16 %2, %9 offset:%c12\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:%c13\n"
+        "ds_read_b64_tr_b16 %4, %10 offset:%c12\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:%c13\n"
+        "ds_read_b64_tr_b16 %6, %11 offset:%c12\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:%c13\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(O0), "i"(O1)
+        : "memory");
+  }
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) vf[n] = join_bf16x4(x[2 * n], x[2 * n + 1]);
+}
 
 // Partials combined per round trip by the last chunk of a cut tile.
 template <int D>
@@ -138,6 +180,7 @@ constexpr int kMinBlocksPerCu = D == 64 ? 3 : 2;
 
 template <int D, bool CAUSAL, bool DYN>
 __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(const PrefillParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   constexpr int KS = D / 16;  // k-steps of the S MFMA
   constexpr int NTD = D / 32; // 32-wide d tiles of the O MFMA
   static_assert(NTD * 16 * NT == BR * D, "one partial = the accumulators of all threads");
@@ -195,6 +238,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     e0 = p.row_ptr ? p.row_ptr[t] : 0;
     e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
   }
+  // the work item is wave-uniform: keep it (and all block-index arithmetic
+  // derived from it) in scalar registers
+  t = __builtin_amdgcn_readfirstlane(t);
+  e0 = __builtin_amdgcn_readfirstlane(e0);
+  e1 = __builtin_amdgcn_readfirstlane(e1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  mrg = __builtin_amdgcn_readfirstlane(mrg);
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
@@ -230,6 +280,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       nblk = max(0, min(nblk, last_row / BC + 1 - e0));
     }
   }
+  nblk = __builtin_amdgcn_readfirstlane(nblk);
 
   const float c2 = p.scale * kLog2e;                    // raw score -> log2 units
   const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
@@ -242,21 +293,22 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   int skipped = 0;
 
   constexpr int ST = kStages<D>;
-  constexpr int DMA_PER_BLOCK = 2 * (D / 32);  // K and V, CH/4 instructions each per wave
+  static_assert(ST == 2, "the block-index prefetch below assumes a two-stage ring");
   auto blk = [&](int i) __attribute__((always_inline)) { return cols ? cols[i] : e0 + i; };
   TileSrc<D, false> ksrc;
   TileSrc<D, true> vsrc;
-  ksrc.init(p.ks_t, wave, lane);
-  vsrc.init(p.vs_t, wave, lane);
-  auto fetch = [&](int i) __attribute__((always_inline)) {
+  ksrc.init(kbase, p.ks_t, p.Nk, wave, lane);
+  vsrc.init(vbase, p.vs_t, p.Nk, wave, lane);
+  auto fetch = [&](int i, int jj) __attribute__((always_inline)) {
     const int stg = i % ST;
-    const int jj = blk(i);
-    ksrc.issue(sm.k[stg], kbase, p.ks_t, jj, p.Nk, wave);
-    vsrc.issue(sm.v[stg], vbase, p.vs_t, jj, p.Nk, wave);
+    ksrc.issue(sm.k[stg], p.ks_t, jj, wave);
+    vsrc.issue(sm.v[stg], p.vs_t, jj, wave);
   };
-#pragma unroll
-  for (int i = 0; i < ST - 1; ++i)
-    if (i < nblk) fetch(i);
+  // key-block indices run two blocks ahead of use, so the CSR read is never
+  // on the path from one block's barrier to the next block's loads
+  int j_cur = nblk > 0 ? __builtin_amdgcn_readfirstlane(blk(0)) : 0;
+  int j_nxt = nblk > 1 ? __builtin_amdgcn_readfirstlane(blk(1)) : 0;
+  if (nblk > 0) fetch(0, j_cur);
 
   const int g16 = lane >> 4, j16 = lane & 15;
   const int vr0 = 4 * (g16 >> 1) + (j16 >> 2);
@@ -265,12 +317,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 
   for (int it = 0; it < nblk; ++it) {
     const int stg = it % ST;
-    const int j = blk(it);
-    // block it has landed once at most the next block's requests are in flight
-    if (ST > 2 && it + 1 < nblk) wait_vmem_le<(ST > 2 ? DMA_PER_BLOCK : 0)>();
-    else wait_vmem_le<0>();
-    __syncthreads();  // block it visible; every wave is done with block it-1's stage
-    if (it + ST - 1 < nblk) fetch(it + ST - 1);
+    const int j = j_cur;
+    wait_vmem_le<0>();  // block it has landed (and the index read below it)
+    __syncthreads();    // block it visible; every wave is done with block it-1's stage
+    if (it + 1 < nblk) fetch(it + 1, j_nxt);
+    const int j_after = it + 2 < nblk ? __builtin_amdgcn_readfirstlane(blk(it + 2)) : 0;
+    j_cur = j_nxt;
+    j_nxt = j_after;
     const __bf16* ktile = sm.k[stg];
     const __bf16* vtile = sm.v[stg];
 
@@ -359,16 +412,22 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         }
       }
       // ---- O^T += V^T P^T : 4 key steps of 16 x NTD d tiles
+      uint32_t vb[NTD];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
+      bf16x8 vf[NTD];
+      read_v_step<D, 0>(vf, vb);
 #pragma unroll
-        for (int n = 0; n < NTD; ++n) {
-          const int r = 16 * kk + vr0, c = 4 * n + vcs;
-          const i16x4 lo = lds_read_tr16(vtile + Tile<D>::vpos(r, c) + vhalf);
-          const i16x4 hi4 = lds_read_tr16(vtile + Tile<D>::vpos(r + 8, c) + vhalf);
-          oacc[n] = mfma32(join_bf16x4(lo, hi4), pf[kk], oacc[n]);
-        }
-      }
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[0], oacc[n]);
+      read_v_step<D, 1>(vf, vb);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[1], oacc[n]);
+      read_v_step<D, 2>(vf, vb);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[2], oacc[n]);
+      read_v_step<D, 3>(vf, vb);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[3], oacc[n]);
     } else {
       ++skipped;
     }
@@ -479,6 +538,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     tc[0] = vis_tot;
     tc[1] = skip_tot;
   }
+#endif
 }
 
 template <int D, bool CAUSAL, bool DYN>

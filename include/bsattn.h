@@ -200,8 +200,9 @@ size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n
  * Validation: pointers non-null and 16-byte aligned, token/head strides
  * multiples of 8 (bf16) or 4 (fp32) elements, d contiguous; CSR pointers
  * both set or both NULL (the CSR itself is not read on the host: call
- * bsattn_validate_block_index on the host copy).  Returns BSATTN_ERR_HIP
- * if the launch fails. */
+ * bsattn_validate_block_index on the host copy); bf16: (Nk + 64) x K/V
+ * token stride x 2 bytes below 4 GiB (32-bit offsets within one head,
+ * else BSATTN_ERR_UNSUPPORTED).  Returns BSATTN_ERR_HIP if the launch fails. */
 bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

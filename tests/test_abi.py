@@ -71,6 +71,8 @@ BAD_PREFILL = [
     ("n_valid > Nk", lambda a: setattr(a, "n_valid", 257), _abi.BSATTN_ERR_INVALID_ARG),
     ("Bc 32", lambda a: setattr(a, "Bc", 32), _abi.BSATTN_ERR_UNSUPPORTED),
     ("bf16 Br 64", lambda a: setattr(a, "Br", 64), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("K extent past 32-bit offsets", lambda a: (setattr(a, "Nk", 1 << 21), setattr(a, "Nq", 1 << 21),
+                                                 a.k_stride.__setitem__(1, 1024)), _abi.BSATTN_ERR_UNSUPPORTED),
 ]
 
 
