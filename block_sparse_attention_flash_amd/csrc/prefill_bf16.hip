@@ -187,7 +187,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -286,7 +286,17 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
   float m_run = kNegInf;   // true running max (raw score units)
   float m_ref = kNegInf;   // reference max used in the exponent (raw units)
-  float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's half of the row sum, four partial sums
+  // Row sums.  At d = 64 the vector ALUs are the busier unit, so the sums run
+  // on the matrix core: an all-ones A operand makes every element of lacc in
+  // lane l the sum of P over the keys of query row l % 32 (the same bf16 P the
+  // numerator uses); only element 0 is read and rescaled.  At d = 128 the
+  // matrix core is the busier one and the sums stay on the vector ALUs.
+  constexpr bool kSumOnMfma = D == 64;
+  f32x16 lacc = f32x16{};
+  float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // vector-ALU form: this lane's half, four partial sums
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
   f32x16 oacc[NTD];
 #pragma unroll
   for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
@@ -308,6 +318,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   // on the path from one block's barrier to the next block's loads
   int j_cur = nblk > 0 ? __builtin_amdgcn_readfirstlane(blk(0)) : 0;
   int j_nxt = nblk > 1 ? __builtin_amdgcn_readfirstlane(blk(1)) : 0;
+  int j_raw = nblk > 2 ? blk(2) : 0;  // loaded a full iteration before it is needed
   if (nblk > 0) fetch(0, j_cur);
 
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -318,10 +329,11 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   for (int it = 0; it < nblk; ++it) {
     const int stg = it % ST;
     const int j = j_cur;
-    wait_vmem_le<0>();  // block it has landed (and the index read below it)
+    wait_vmem_le<0>();  // block it has landed (and the index read last iteration)
     __syncthreads();    // block it visible; every wave is done with block it-1's stage
+    const int j_after = __builtin_amdgcn_readfirstlane(j_raw);
     if (it + 1 < nblk) fetch(it + 1, j_nxt);
-    const int j_after = it + 2 < nblk ? __builtin_amdgcn_readfirstlane(blk(it + 2)) : 0;
+    j_raw = it + 3 < nblk ? blk(it + 3) : 0;
     j_cur = j_nxt;
     j_nxt = j_after;
     const __bf16* ktile = sm.k[stg];
@@ -360,12 +372,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     }
 
     // ---- block row max and running max
-    float mb = kNegInf;
+    float mb0 = kNegInf, mb1 = kNegInf;  // two independent chains
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) mb = fmaxf(mb, sacc[mt][a]);
-    mb = wave_max_xor32(mb);
+    for (int a = 0; a < 16; ++a) {
+      mb0 = fmaxf(mb0, sacc[0][a]);
+      mb1 = fmaxf(mb1, sacc[1][a]);
+    }
+    const float mb = wave_max_xor32(fmaxf(mb0, mb1));
     const float m_new = fmaxf(m_run, mb);
 
     bool skip = false;
@@ -387,8 +400,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       if (__any(need)) {
         const float alpha = need ? ((m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c2)) : 1.0f;
         if (need) m_ref = m_new;
+        if constexpr (kSumOnMfma) {
+          lacc[0] *= alpha;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l4[i] *= alpha;
+          for (int i = 0; i < 4; ++i) l4[i] *= alpha;
+        }
 #pragma unroll
         for (int n = 0; n < NTD; ++n)
 #pragma unroll
@@ -404,9 +421,8 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
           float pv[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float e = fast_exp2(fmaf(sacc[mt][8 * hf + i], c2, -mref2));
-            pv[i] = e;
-            l4[i & 3] += e;
+            pv[i] = fast_exp2(fmaf(sacc[mt][8 * hf + i], c2, -mref2));
+            if constexpr (!kSumOnMfma) l4[i & 3] += pv[i];
           }
           pf[2 * mt + hf] = to_bf16x8(pv);
         }
@@ -419,21 +435,30 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       read_v_step<D, 0>(vf, vb);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[0], oacc[n]);
+      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[0], lacc);
       read_v_step<D, 1>(vf, vb);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[1], oacc[n]);
+      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[1], lacc);
       read_v_step<D, 2>(vf, vb);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[2], oacc[n]);
+      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[2], lacc);
       read_v_step<D, 3>(vf, vb);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[3], oacc[n]);
+      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[3], lacc);
     } else {
       ++skipped;
     }
   }
-  const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
-  float l_tot = l_part + __shfl_xor(l_part, 32);
+  float l_tot;
+  if constexpr (kSumOnMfma) {
+    l_tot = lacc[0];
+  } else {
+    const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    l_tot = l_part + __shfl_xor(l_part, 32);
+  }
   int vis_tot = nblk, skip_tot = skipped;
 
   if (slot >= 0) {
