@@ -69,9 +69,10 @@ struct Tile {
   __device__ static __forceinline__ int vpos(int r, int c) { return (r * CH + (c ^ vxor(r))) * 8; }
 };
 
-// K/V ring in LDS: two stages (block j+1 streams in while block j is used).
-// A third stage at d = 64 measured slower: the deeper ring costs occupancy
-// that the extra lead time does not repay.  The loop below supports any depth.
+// K/V ring in LDS: two stages (block j+1 streams in during all of block j's
+// work).  The loop also runs three (block j+2 requested while j is used); at
+// d = 64 that measured no faster (0.0648 against 0.0639 ms on the DiT
+// image+text workload), and at d = 128 it would not fit two work-groups per CU.
 template <int D>
 constexpr int kStages = 2;
 
@@ -172,6 +173,12 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Work-group barrier without the memory fence of __syncthreads (whose
+// vmcnt(0) would also wait for the K/V blocks still streaming in).  Every
+// wait it relies on is explicit: the block's own loads (vmcnt), and the LDS
+// reads of the previous block, which each wave waits for before using them.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Work-groups per CU the register budget is cut for: three at d = 64 (at most
 // 168 VGPRs), two at d = 128 (at most 256).
@@ -303,8 +310,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   int skipped = 0;
 
   constexpr int ST = kStages<D>;
-  static_assert(ST == 2, "the block-index prefetch below assumes a two-stage ring");
-  auto blk = [&](int i) __attribute__((always_inline)) { return cols ? cols[i] : e0 + i; };
+  constexpr int DMA_PER_BLOCK = 2 * (D / 32);  // K and V loads of one block, per wave
+  // CSR entries through the scalar cache (wave-uniform, read-only here), so
+  // they never share the vector-memory counter with the K/V loads
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr ccols = cols ? (const_i32_ptr)(cols) : nullptr;
+  auto blk = [&](int i) __attribute__((always_inline)) { return i < nblk ? (ccols ? ccols[i] : e0 + i) : 0; };
   TileSrc<D, false> ksrc;
   TileSrc<D, true> vsrc;
   ksrc.init(kbase, p.ks_t, p.Nk, wave, lane);
@@ -314,12 +325,11 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     ksrc.issue(sm.k[stg], p.ks_t, jj, wave);
     vsrc.issue(sm.v[stg], p.vs_t, jj, wave);
   };
-  // key-block indices run two blocks ahead of use, so the CSR read is never
-  // on the path from one block's barrier to the next block's loads
-  int j_cur = nblk > 0 ? __builtin_amdgcn_readfirstlane(blk(0)) : 0;
-  int j_nxt = nblk > 1 ? __builtin_amdgcn_readfirstlane(blk(1)) : 0;
-  int j_raw = nblk > 2 ? blk(2) : 0;  // loaded a full iteration before it is needed
-  if (nblk > 0) fetch(0, j_cur);
+  // block indices of blocks it .. it+3; the farthest is read a full iteration
+  // (two at two stages) before its loads are issued
+  int q0 = blk(0), q1 = blk(1), q2 = blk(2), q3 = ST == 3 ? blk(3) : 0;
+  if (nblk > 0) fetch(0, q0);
+  if (ST == 3 && nblk > 1) fetch(1, q1);
 
   const int g16 = lane >> 4, j16 = lane & 15;
   const int vr0 = 4 * (g16 >> 1) + (j16 >> 2);
@@ -328,14 +338,20 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 
   for (int it = 0; it < nblk; ++it) {
     const int stg = it % ST;
-    const int j = j_cur;
-    wait_vmem_le<0>();  // block it has landed (and the index read last iteration)
-    __syncthreads();    // block it visible; every wave is done with block it-1's stage
-    const int j_after = __builtin_amdgcn_readfirstlane(j_raw);
-    if (it + 1 < nblk) fetch(it + 1, j_nxt);
-    j_raw = it + 3 < nblk ? blk(it + 3) : 0;
-    j_cur = j_nxt;
-    j_nxt = j_after;
+    const int j = q0;
+    // block it has landed once at most the next block's loads are in flight
+    // (block-state stores, when requested, also count: then wait for all)
+    if (ST == 3 && it + 1 < nblk && !p.block_state) wait_vmem_le<(ST == 3 ? DMA_PER_BLOCK : 0)>();
+    else wait_vmem_le<0>();
+    block_barrier();  // block it visible; every wave is done with block it-1's stage
+    // lgkmcnt(0): the block index read at the end of the last iteration has
+    // long arrived; saying so (through the builtin the compiler tracks) keeps
+    // its scalar load from coarsening the K-fragment waits below
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (it + ST - 1 < nblk) fetch(it + ST - 1, ST == 3 ? q2 : q1);
+    q0 = q1;
+    q1 = q2;
+    if constexpr (ST == 3) q2 = q3;
     const __bf16* ktile = sm.k[stg];
     const __bf16* vtile = sm.v[stg];
 
@@ -386,7 +402,8 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       const bool agree = (mb == kNegInf) || ((mb - m_new) * c2 < log2_lambda);
       const bool wave_all = __all(agree);
       if (lane == 0) sm.vote[it & 1][wave] = wave_all ? 1 : 0;
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the vote word is in LDS
+      block_barrier();
       const int* vt = sm.vote[it & 1];
       skip = (vt[0] & vt[1] & vt[2] & vt[3]) != 0;
     }
@@ -451,6 +468,10 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     } else {
       ++skipped;
     }
+    // the farthest block index, read through the scalar cache after this
+    // block's LDS traffic (its wait then costs nothing where it is used)
+    if constexpr (ST == 3) q3 = blk(it + 4);
+    else q2 = blk(it + 3);
   }
   float l_tot;
   if constexpr (kSumOnMfma) {
