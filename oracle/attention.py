@@ -206,6 +206,37 @@ def skip_set_vectorized(qr, k, rows, blocks, Bc: int, scale: float, lam: float,
     return skip, bm
 
 
+def row_agreement(qr, k, rows, blocks, Bc: int, scale: float, lam: float, n_valid: int, causal: bool):
+    """Per-row form of the BLASST skip condition, for the per-row against
+    tile-wide comparison: walk the visited blocks as Algorithm 1 does (running
+    max updated with the block maximum before the test) and, for every block,
+    count the rows of the tile whose own condition holds (block max - running
+    max < ln(lambda), or no allowed key in the block), before the tile-wide
+    reduction of BLASST notes section 4.
+
+    Returns (agree [nb] int counts, gap [R, nb]) with gap the row's block max
+    minus its running max in natural-log units (-inf where the row has no
+    allowed key in the block).  lambda = 0 counts nothing (no test is made)."""
+    qr, k = as_f64(qr), as_f64(k)
+    lnl = log_threshold(lam)
+    n_k = k.shape[0]
+    R = qr.shape[0]
+    m = np.full(R, -np.inf)
+    agree = np.zeros(len(blocks), dtype=np.int64)
+    gaps = np.full((R, len(blocks)), -np.inf)
+    for pos, j in enumerate(blocks):
+        keys = block_keys(int(j), Bc, n_k)
+        allowed = allowed_entries(rows, keys, n_valid, causal)
+        S = np.where(allowed, scale * (qr @ k[keys].T), -np.inf)
+        m_blk = S.max(axis=1)
+        m = np.maximum(m, m_blk)
+        finite = np.isfinite(m_blk)
+        gaps[finite, pos] = m_blk[finite] - m[finite]
+        if lam > 0.0:
+            agree[pos] = int(np.count_nonzero(~finite | (gaps[:, pos] < lnl)))
+    return agree, gaps
+
+
 def static_tile(qr, k, v, rows, blocks, Bc: int, scale: float, n_valid: int, causal: bool):
     """Block-sparse attention for one tile: plain masked softmax over the keys of
     the tile's visited blocks (two-pass; equal to the online form)."""

@@ -188,6 +188,45 @@ def test_skip_loop_equals_cummax_form(lam):
 
 # ---- C-P6: monotone in lambda, first block never skipped --------------------
 
+def _row_agree_brute(qr, k, rows, blocks, Bc, scale, lam, n_valid, causal):
+    """Per-row skip condition by plain loops over rows, blocks and keys."""
+    cnt = []
+    run = [-math.inf] * len(rows)
+    for j in blocks:
+        c = 0
+        for a, r in enumerate(rows):
+            best = -math.inf
+            for key in range(j * Bc, min((j + 1) * Bc, k.shape[0])):
+                if key < n_valid and (not causal or key <= r):
+                    best = max(best, scale * float(np.dot(qr[a], k[key])))
+            run[a] = max(run[a], best)
+            if best == -math.inf or best - run[a] < math.log(lam):
+                c += 1
+        cnt.append(c)
+    return cnt
+
+
+@pytest.mark.parametrize("lam", [0.05, 0.4, 0.9])
+def test_row_agreement_brute_force_and_invariants(lam):
+    cfg, (q, k, v) = _concentrated_case(L=160, Hq=2, Hkv=1, d=16)
+    for h in range(2):
+        for t in range(3):
+            rows = A.tile_rows(t, 64, 160)
+            blocks = A.visited_blocks(t, 64, 32, 160, 160, True)
+            qr = A.as_f64(q[0, rows[0]:rows[-1] + 1, h])
+            kk = A.as_f64(k[0, :, 0])
+            agree, gaps = A.row_agreement(qr, kk, rows, blocks, 32, 0.25, lam, 160, True)
+            assert agree.tolist() == _row_agree_brute(qr, kk, rows, blocks, 32, 0.25, lam, 160, True)
+            _, skip, _ = A.blasst_tile(qr, kk, A.as_f64(v[0, :, 0]), rows, blocks, 32, 0.25, lam, 160, True)
+            assert all(agree[skip] == len(rows))            # a skipped block: every row agrees
+            assert all(agree[~skip] < len(rows))            # a kept block: some row disagrees
+            assert agree[0] == np.count_nonzero(~np.isfinite(gaps[:, 0]))   # first block: gap 0 for live rows
+    # lambda -> 0+: only rows with no allowed key in the block agree; lambda = 0 counts nothing
+    agree, gaps = A.row_agreement(qr, kk, rows, blocks, 32, 0.25, 1e-300, 160, True)
+    assert agree.tolist() == np.count_nonzero(~np.isfinite(gaps), axis=0).tolist()
+    assert A.row_agreement(qr, kk, rows, blocks, 32, 0.25, 0.0, 160, True)[0].sum() == 0
+
+
 def test_skip_monotone_and_first_block_kept():
     cfg, (q, k, v) = _concentrated_case()
     prev = None
