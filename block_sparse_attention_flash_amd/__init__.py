@@ -216,8 +216,8 @@ class Plan:
 
 def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                  Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
-                 out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
-                 workspace=None) -> Plan:
+                 out=None, tile_counters=None, block_state=None, row_counters=None,
+                 schedule: Optional[Schedule] = None, workspace=None) -> Plan:
     """Marshal a prefill (arguments as ``prefill_fwd``) into a reusable Plan."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
@@ -248,6 +248,7 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
     a.causal = 1 if causal else 0
     a.Br, a.Bc = int(Br), int(Bc)
     a.tile_counters, a.block_state = _ptr(tile_counters), _ptr(block_state)
+    a.row_counters = _ptr(row_counters)
     if schedule is not None:
         if schedule.d_items is None:
             schedule.to(q.device)
@@ -258,25 +259,27 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
                 workspace = prefill_workspace(B, Hq, d, schedule.n_slots, q.device)
             a.workspace = _ptr(workspace)
             a.workspace_bytes = int(workspace.numel() * workspace.element_size())
-    keep = (q, k, v, row_ptr, col_idx, tile_order, tile_counters, block_state, schedule, workspace)
+    keep = (q, k, v, row_ptr, col_idx, tile_order, tile_counters, block_state, row_counters, schedule, workspace)
     return Plan(library().bsattn_prefill_fwd, a, out, keep)
 
 
 def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                 Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
-                out=None, tile_counters=None, block_state=None, schedule: Optional[Schedule] = None,
-                workspace=None, stream=None):
+                out=None, tile_counters=None, block_state=None, row_counters=None,
+                schedule: Optional[Schedule] = None, workspace=None, stream=None):
     """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
 
     ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
     ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
-    [B, Hq, Tr, Tc] are optional device outputs.  ``schedule`` (from
+    [B, Hq, Tr, Tc] are optional device outputs, as is ``row_counters`` int32
+    [B, Hq, Tr] (per-row skip conditions that held, for lambda > 0).  ``schedule`` (from
     ``build_schedule``, device copies made with ``.to``) cuts long tiles;
     its partials go to ``workspace`` (a uint8 device tensor from
     ``prefill_workspace``, allocated here if None).  Returns ``out``."""
     return prefill_plan(q, k, v, scale=scale, lam=lam, causal=causal, Br=Br, Bc=Bc, row_ptr=row_ptr,
                         col_idx=col_idx, tile_order=tile_order, n_valid=n_valid, out=out,
-                        tile_counters=tile_counters, block_state=block_state, schedule=schedule,
+                        tile_counters=tile_counters, block_state=block_state, row_counters=row_counters,
+                        schedule=schedule,
                         workspace=workspace)(stream)
 
 

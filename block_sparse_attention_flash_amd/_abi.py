@@ -48,6 +48,7 @@ class PrefillArgs(C.Structure):
                 ("n_valid", C.c_int32), ("scale", C.c_float), ("lam", C.c_float), ("causal", C.c_int32),
                 ("Br", C.c_int32), ("Bc", C.c_int32),
                 ("tile_counters", C.c_void_p), ("block_state", C.c_void_p),
+                ("row_counters", C.c_void_p),
                 ("sched_items", C.c_void_p), ("n_items", C.c_int32), ("sched_merges", C.c_void_p),
                 ("n_merges", C.c_int32), ("n_slots", C.c_int32), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t)]

@@ -172,6 +172,7 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   p.Tr = (a->Nq + a->Br - 1) / a->Br;
   p.Tc = (a->Nk + a->Bc - 1) / a->Bc;
   p.tile_counters = a->tile_counters; p.block_state = a->block_state;
+  p.row_counters = a->row_counters;
   if (a->sched_items) {
     if (a->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "schedules are implemented for the bf16 path");
     if (!a->row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a schedule needs the CSR (row_ptr, col_idx)");

@@ -38,6 +38,7 @@ struct PrefillParams {
   int32_t Tr, Tc;
   int32_t* tile_counters;
   uint8_t* block_state;
+  int32_t* row_counters;
   const int32_t* sched_items;   // [n_items][5] or NULL
   int32_t n_items;
   const int32_t* sched_merges;  // [n_merges][3]

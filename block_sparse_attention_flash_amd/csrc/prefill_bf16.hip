@@ -308,6 +308,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 #pragma unroll
   for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
   int skipped = 0;
+  int rows_agree = 0;  // row conditions that held (this wave's rows), for row_counters
 
   constexpr int ST = kStages<D>;
   constexpr int DMA_PER_BLOCK = 2 * (D / 32);  // K and V loads of one block, per wave
@@ -401,6 +402,8 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     if (DYN) {
       const bool agree = (mb == kNegInf) || ((mb - m_new) * c2 < log2_lambda);
       const bool wave_all = __all(agree);
+      // lanes l and l + 32 hold the same row: count the wave's 32 rows once
+      if (p.row_counters) rows_agree += __popcll(__ballot(agree && row_ok) & 0xffffffffull);
       if (lane == 0) sm.vote[it & 1][wave] = wave_all ? 1 : 0;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the vote word is in LDS
       block_barrier();
@@ -583,6 +586,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
     tc[0] = vis_tot;
     tc[1] = skip_tot;
+  }
+  if (p.row_counters) {  // the tile's four waves: one LDS word each (the vote words are free now)
+    __syncthreads();
+    if (lane == 0) sm.vote[0][wave] = rows_agree;
+    __syncthreads();
+    if (tid == 0)
+      p.row_counters[((int64_t)b * p.Hq + h) * p.Tr + t] = sm.vote[0][0] + sm.vote[0][1] + sm.vote[0][2] + sm.vote[0][3];
   }
 #endif
 }

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(BR) void prefill_f32_kernel(const PrefillParams p) 
     beg = p.row_ptr[t];
     end = p.row_ptr[t + 1];
   }
-  int visited = 0, skipped = 0;
+  int visited = 0, skipped = 0, rows_agree = 0;
   for (int e = beg; e < end; ++e) {
     const int j = p.row_ptr ? p.col_idx[e] : e;
     if (p.causal && j * BC > last_row) break;  // ascending: nothing further is visited
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(BR) void prefill_f32_kernel(const PrefillParams p) 
     if (dyn) {
       const bool agree = (m_blk == kNegInf) || (m_blk - m_new < ln_lambda);
       skip = __syncthreads_and(agree) != 0;
+      if (p.row_counters) rows_agree += __syncthreads_count(agree && row_ok);
     }
     if (p.block_state && tid == 0) {
       const int64_t bs = (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j;
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(BR) void prefill_f32_kernel(const PrefillParams p) 
     tc[0] = visited;
     tc[1] = skipped;
   }
+  if (p.row_counters && tid == 0) p.row_counters[((int64_t)b * p.Hq + h) * p.Tr + t] = rows_agree;
 }
 
 template <int D, int BR>

@@ -178,6 +178,12 @@ typedef struct {
   int32_t* tile_counters; /* optional device [B, Hq, Tr, 2] int32: {visited, skipped} blocks */
   uint8_t* block_state;   /* optional device [B, Hq, Tr, Tc]: the kernel writes 1 (computed) or
                              2 (skipped) for visited blocks; the caller zero-fills it first */
+  int32_t* row_counters;  /* optional device [B, Hq, Tr] int32: for lambda > 0, the number of
+                             (query row < Nq, visited block) pairs whose own row condition
+                             holds (block max - running max < ln lambda, or no allowed key),
+                             before the tile-wide vote (BLASST notes sections 3.1.1 and 4);
+                             0 for lambda = 0.  Compare with skipped x rows for the cost of
+                             tile-wide decisions */
   const int32_t* sched_items;  /* optional device copy of bsattn_build_schedule's items (needs the CSR);
                                   NULL = one work-group per tile (tile_order applies) */
   int32_t n_items;

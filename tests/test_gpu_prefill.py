@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import block_sparse_attention_flash_amd as bsa
+from oracle import attention as A
 from oracle import masks as M
 from workloads import get_config, gen_prefill_inputs
 from workloads.configs import PrefillWorkload, dit_image_text_spec, video_text_spec
@@ -293,3 +294,49 @@ def test_prefill_plan_and_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(plan.out, ref), r
     del junk
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("fp32", 64)])
+def test_row_counters_match_oracle(dtype, d):
+    """Per-row skip conditions counted by the kernel (before the tile-wide vote)
+    equal the oracle's count, except (row, block) pairs whose gap lies within
+    the excused band around ln(lambda); with a static CSR and dynamic skipping
+    together."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13
+    for lam, gen, csr_on, causal in ((0.3, "sink", False, True), (0.05, "concentrated", True, False),
+                                     (0.6, "sink", True, False)):
+        cfg = _small("rows", dtype=dtype, N=n, d=d, Hq=4, Hkv=2, causal=causal, lam=lam, generator=gen, seed=12)
+        Br = 128 if dtype == "bf16" else 64
+        _say(f"row counters {dtype} d{d} lambda {lam} {gen} csr={csr_on} causal={causal}")
+        q, k, v = gen_prefill_inputs(cfg)
+        csr = bsa.build_block_index(spec, n, n, Br, 64) if csr_on else None
+        Tr = -(-n // Br)
+        rc = torch.full((cfg.B, cfg.Hq, Tr), -1, dtype=torch.int32, device=DEV)
+        rp = ci = None
+        if csr is not None:
+            rp, ci = torch.from_numpy(csr[0]).to(DEV), torch.from_numpy(csr[1]).to(DEV)
+        bsa.prefill_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=cfg.scale, lam=lam, causal=causal, Br=Br, Bc=64,
+                        row_ptr=rp, col_idx=ci, n_valid=spec.n_valid, row_counters=rc)
+        torch.cuda.synchronize()
+        rc = rc.cpu().numpy()
+        total = 0
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                g = A.kv_head_of(h, cfg.Hq, cfg.Hkv)
+                for t in range(Tr):
+                    rows = A.tile_rows(t, Br, n)
+                    blocks = A.visited_blocks(t, Br, 64, n, n, causal, *(csr if csr is not None else (None, None)))
+                    qr = A.as_f64(q[b, rows[0]:rows[-1] + 1, h])
+                    agree, gaps = A.row_agreement(qr, k[b, :, g], rows, blocks, 64, cfg.scale, lam, spec.n_valid,
+                                                  causal)
+                    near = int(np.count_nonzero(np.abs(gaps - np.log(lam)) <= 1e-3))
+                    assert abs(int(rc[b, h, t]) - int(agree.sum())) <= near, (b, h, t, rc[b, h, t], agree.sum(), near)
+                    total += int(agree.sum())
+        assert total > 0
+    # lambda = 0: no test is made, nothing counted
+    rc0 = torch.full((cfg.B, cfg.Hq, Tr), -1, dtype=torch.int32, device=DEV)
+    bsa.prefill_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=cfg.scale, lam=0.0, Br=Br, Bc=64, row_ptr=rp,
+                    col_idx=ci, n_valid=spec.n_valid, row_counters=rc0)
+    torch.cuda.synchronize()
+    assert int(rc0.cpu().abs().sum()) == 0
