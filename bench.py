@@ -244,6 +244,114 @@ def run_decode_workload(name: str, steps: int, warmup: int):
     return res
 
 
+# ---------------------------------------------------------------------------- lambda sweep
+
+SWEEP_LAMBDAS = {
+    "cfg4": [0.0, 40.0 / 32768, 1e-2, 3e-2, 0.1, 0.2, 0.3, 0.5],
+    "cfg2": [0.0, 1e-2, 0.05, 0.1, 0.3],
+    "cfg3": [0.0, 1e-2, 0.1, 0.3],
+    "cfg5": [0.0, 40.0 / 131072, 1e-3, 1e-2, 0.1],
+}
+
+
+def sweep_prefill(name: str, lams, steps: int, warmup: int):
+    """BLASST over each workload's visited blocks (the static CSR when the
+    workload has a mask: static and dynamic skipping together) at several
+    lambda; per lambda the time, the tile skip share, and the share of
+    (row, visited block) pairs whose own row condition held."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_prefill_inputs
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"sweep {name}: generating inputs ({cfg.description})")
+    q, k, v = gen_prefill_inputs(cfg, device=dev)
+    Tr, Tc = -(-cfg.N // cfg.Br), -(-cfg.N // cfg.Bc)
+    rows_per_tile = np.minimum(cfg.Br, cfg.N - np.arange(Tr) * cfg.Br)
+    rp = ci = order = sched = ws = None
+    if cfg.mask is not None:
+        rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
+        order_h = bsa.tile_order_lpt(rp_h)
+        sched = bsa.build_schedule(rp_h, bsa.default_max_blocks_per_item(rp_h, cfg.B, cfg.Hq)).to(dev)
+        rp, ci, order = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, order_h))
+        if sched.n_slots:
+            ws = bsa.prefill_workspace(cfg.B, cfg.Hq, cfg.d, sched.n_slots, dev)
+    out = torch.empty_like(q)
+    res = []
+    base_ms = None
+    for lam in lams:
+        use_sched = sched if lam == 0.0 else None  # cut tiles are exact only for lambda = 0
+        cnt = torch.zeros((cfg.B, cfg.Hq, Tr, 2), dtype=torch.int32, device=dev)
+        rowc = torch.zeros((cfg.B, cfg.Hq, Tr), dtype=torch.int32, device=dev)
+
+        def plan(c=None, r=None):
+            return bsa.prefill_plan(q, k, v, scale=cfg.scale, lam=lam, causal=cfg.causal, Br=cfg.Br, Bc=cfg.Bc,
+                                    row_ptr=rp, col_idx=ci, tile_order=order, n_valid=cfg.n_valid, out=out,
+                                    tile_counters=c, row_counters=r, schedule=use_sched, workspace=ws)
+
+        plan(cnt, rowc)()
+        torch.cuda.synchronize()
+        c = cnt.cpu().numpy().astype(np.int64)
+        rc = rowc.cpu().numpy().astype(np.int64)
+        t = time_launches(plan(), steps, warmup)
+        ms = t["ms_per_step"]
+        base_ms = ms if base_ms is None else base_ms
+        visited, skipped = int(c[..., 0].sum()), int(c[..., 1].sum())
+        pairs = int((c[..., 0] * rows_per_tile).sum())
+        pairs_tile = int((c[..., 1] * rows_per_tile).sum())
+        per_block = 2 * cfg.Br * cfg.Bc * cfg.d
+        pairs_dense = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.n_valid
+        res.append({"lambda": lam, "ms": ms, "speedup_vs_lambda0": base_ms / ms,
+                    "pct_blocks_skipped": 100.0 * skipped / max(1, visited),
+                    "pct_rows_condition_held": 100.0 * int(rc.sum()) / max(1, pairs) if lam > 0 else 0.0,
+                    "pct_rows_in_skipped_blocks": 100.0 * pairs_tile / max(1, pairs),
+                    "dense_equiv_tflops": 4 * cfg.B * cfg.Hq * cfg.d * pairs_dense / (ms * 1e-3) / 1e12,
+                    "processed_tflops": per_block * (2 * visited - skipped) / (t["per_launch_avg_ms"] * 1e-3) / 1e12,
+                    "schedule": use_sched is not None})
+        log(f"sweep {name} lambda {lam:.3g}: {ms:.4f} ms, skipped {res[-1]['pct_blocks_skipped']:.2f}% of blocks, "
+            f"row condition held for {res[-1]['pct_rows_condition_held']:.2f}% of (row, block) pairs")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"workload": name, "description": cfg.description, "points": res}
+
+
+def sweep_decode(name: str, lams, steps: int, warmup: int):
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_decode_inputs
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"sweep {name}: generating inputs ({cfg.description})")
+    q, kc, vc = gen_decode_inputs(cfg, device=dev)
+    ws = bsa.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, dev, cfg.Bc)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.bfloat16, device=dev)
+    res = []
+    base_ms = None
+    for lam in lams:
+        cnt = torch.zeros((cfg.B, cfg.Hkv, 2), dtype=torch.int32, device=dev)
+        mk = lambda c=None: bsa.decode_plan(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=lam, Bc=cfg.Bc, workspace=ws,
+                                            out=out, counters=c)
+        mk(cnt)()
+        torch.cuda.synchronize()
+        c = cnt.view(-1, 2).sum(0).tolist()
+        visited, skipped = int(c[0]), int(c[1])
+        t = time_launches(mk(), steps, warmup)
+        ms = t["ms_per_step"]
+        base_ms = ms if base_ms is None else base_ms
+        blk = cfg.Bc * cfg.d * 2
+        algo = visited * blk + (visited - skipped) * blk + 2 * cfg.B * cfg.Hq * cfg.d * 2
+        res.append({"lambda": lam, "ms": ms, "speedup_vs_lambda0": base_ms / ms,
+                    "pct_blocks_skipped": 100.0 * skipped / max(1, visited), "algorithmic_GBs": algo / (ms * 1e-3) / 1e9,
+                    "health": bsa.decode_check(ws)})
+        log(f"sweep {name} lambda {lam:.3g}: {ms:.4f} ms, skipped {res[-1]['pct_blocks_skipped']:.2f}%")
+    del q, kc, vc, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": name, "description": cfg.description, "points": res}
+
+
 # ---------------------------------------------------------------------------- oracle on host cores
 
 def cpu_baseline_prefill(res, budget_s: float):
@@ -300,6 +408,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="one work-group per tile (no long-tile cutting)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the metric line: a lambda sweep (static + dynamic skipping together) per "
+                         "workload, as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
@@ -320,6 +431,14 @@ def main(argv=None) -> int:
         return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep, use_schedule=not a.no_schedule)
 
     torch.cuda.synchronize()
+    if a.sweep:
+        rep = []
+        for name, lams in SWEEP_LAMBDAS.items():
+            fn = sweep_decode if name == "cfg5" else sweep_prefill
+            rep.append(fn(name, lams, min(a.steps, 50) if name != "cfg2" else a.steps, min(a.warmup, 20)
+                          if name != "cfg2" else a.warmup))
+        print(json.dumps({"sweep": rep, "steps": a.steps, "device": torch.cuda.get_device_name(0)}))
+        return 0
     if a.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         dst = torch.empty_like(src)
