@@ -354,6 +354,171 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   }
 }
 
+// lambda = 0: nothing is decided, so a split needs neither the block maxima
+// pass nor the look-back.  One pass: each wave streams K and V of its blocks
+// together, keeps an online softmax per row (running max, rescale; attention
+// tutorial section 4.2), and the four waves merge in LDS into the split's
+// partial, in the layout the combine kernel reads.
+template <int D, int G>
+struct DenseSmem {
+  float pbuf[4][G][64];  // per-wave P of the block in flight
+  float alpha[4][G];     // per-wave rescale of the current block
+  float wm[4][G];        // per-wave final running max (log2 units)
+  float wl[4][G];        // per-wave row sums
+  float obuf[4][G][D];
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(NT) void decode_dense_kernel(const DecodeParams p, DecodeWorkspace wl) {
+  __shared__ DenseSmem<D, G> sm;
+  constexpr int KS = D / 32;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  char* ws = static_cast<char*>(p.workspace);
+  float* stats = reinterpret_cast<float*>(ws + wl.stats);
+  float* accw = reinterpret_cast<float*>(ws + wl.acc);
+  int* counts = reinterpret_cast<int*>(ws + wl.counts);
+  const int S = p.num_splits;
+  const int pair = blockIdx.x / S, s = blockIdx.x % S;
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int unit = pair * S + s;
+  const int blk0 = s * p.blocks_per_split;
+  const int nb = min(p.blocks_per_split, p.Tc - blk0);
+  const float c2 = p.scale * kLog2e;
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+
+  const int r16 = lane & 15, q16 = lane >> 4;
+  bf16x8 qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qa[ks] = r16 < G ? *reinterpret_cast<const bf16x8*>(qbase + (int64_t)(g * G + r16) * p.qs_h + 32 * ks + 8 * q16)
+                     : bf16x8{};
+
+  constexpr int DCH = D / 8;     // 16-byte chunks per key row
+  constexpr int KPS = 64 / DCH;  // keys per load step across the wave
+  constexpr int STEPS = BC / KPS;
+  const int dch = lane % DCH, kg = lane / DCH;
+  float acc[G][8];
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
+  float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // rows 4*q16+i, keys of this lane
+  float mrun[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+
+  for (int lb = wave; lb < nb; lb += 4) {
+    const int j = blk0 + lb;
+    bf16x8 kf[4][KS];
+    load_k_block<D>(kf, kbase, p.ks_t, j, p.L, r16, q16);
+    u32x4 vv[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int key = j * BC + st * KPS + kg;
+      vv[st] = key < p.L ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.ks_t + 8 * dch) : u32x4{0, 0, 0, 0};
+    }
+    f32x4 sc[4];
+    block_scores<D>(sc, kf, qa, c2, j, p.L, r16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+      x = fmaxf(x, __shfl_xor(x, 1));
+      x = fmaxf(x, __shfl_xor(x, 2));
+      x = fmaxf(x, __shfl_xor(x, 4));
+      x = fmaxf(x, __shfl_xor(x, 8));
+      const float m_new = fmaxf(mrun[i], x);
+      const float alpha = mrun[i] == kNegInf ? 0.0f : fast_exp2(mrun[i] - m_new);
+      const float mref = m_new == kNegInf ? 0.0f : m_new;
+      mrun[i] = m_new;
+      lpart[i] *= alpha;
+      const int row = 4 * q16 + i;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float e = fast_exp2(sc[kt][i] - mref);  // 2^-inf = 0 past L
+        lpart[i] += e;
+        if (row < G) sm.pbuf[wave][row][16 * kt + r16] = e;
+      }
+      if (r16 == 0 && row < G) sm.alpha[wave][row] = alpha;
+    }
+    lds_fence();
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float a = sm.alpha[wave][r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] *= a;
+    }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int kl = st * KPS + kg;
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = bf16_bits_to_float(vv[st][e] & 0xffffu);
+        vf[2 * e + 1] = bf16_bits_to_float(vv[st][e] >> 16);
+      }
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const float pr = sm.pbuf[wave][r][kl];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pr, vf[e], acc[r][e]);
+      }
+    }
+    lds_fence();
+  }
+  // per-wave row stats and outputs to LDS
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = lpart[i];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    const int row = 4 * q16 + i;
+    if (r16 == 0 && row < G) {
+      sm.wl[wave][row] = x;
+      sm.wm[wave][row] = mrun[i];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int o = DCH; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o);
+  if (kg == 0) {
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.obuf[wave][r][8 * dch + e] = acc[r][e];
+  }
+  __syncthreads();
+  // merge the waves: M = max m_w, O = sum 2^(m_w - M) O_w, l = sum 2^(m_w - M) l_w
+  for (int x = tid; x < G * D; x += NT) {
+    const int r = x / D, c = x % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.wm[w][r]);
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sm.wm[w][r] != kNegInf) o = fmaf(fast_exp2(sm.wm[w][r] - M), sm.obuf[w][r][c], o);
+    accw[((int64_t)unit * G + r) * D + c] = o;
+  }
+  if (tid < G) {
+    float M = kNegInf, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.wm[w][tid]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sm.wm[w][tid] != kNegInf) l = fmaf(fast_exp2(sm.wm[w][tid] - M), sm.wl[w][tid], l);
+    stats[((int64_t)unit * G + tid) * 2 + 0] = M;
+    stats[((int64_t)unit * G + tid) * 2 + 1] = l;
+  }
+  if (tid == 0) counts[unit] = 0;
+  if (p.block_state)
+    for (int lb = tid; lb < nb; lb += NT) p.block_state[((int64_t)b * p.Hkv + g) * p.Tc + blk0 + lb] = 1;
+}
+
 // Merge the S split partials of one (sequence, query head); write bf16 output
 // and the per-(sequence, K/V head) counters.  256 threads: NT/D groups of D
 // threads walk disjoint split subsets, then the groups are summed.
@@ -425,7 +590,10 @@ template <int D, int G>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const DecodeWorkspace wl = decode_workspace_layout(p.B, p.Hq, p.Hkv, p.d, p.num_splits);
   const int units = p.B * p.Hkv * p.num_splits;
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
+  if (p.lambda > 0.0f)
+    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
+  else
+    hipLaunchKernelGGL((decode_dense_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.Hq), dim3(NT), 0, s, p, wl);
