@@ -352,6 +352,52 @@ def sweep_decode(name: str, lams, steps: int, warmup: int):
     return {"workload": name, "description": cfg.description, "points": res}
 
 
+def calibration_demo(target: float = 0.5, delta: float = 0.05):
+    """BLASST threshold calibration (notes section 3.2, Algorithm 2) on the
+    synthetic decode recipe at several context lengths, and the comparison
+    the notes make in their Table 5: sparsity at the calibrated lambda = a / L
+    against one fixed lambda (the best one at the middle length)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import gen_decode_inputs
+    from workloads.configs import DecodeWorkload
+
+    lengths = [4096, 8192, 16384, 32768, 65536]
+    lambdas = list(np.geomspace(1e-9, 1e-2, 43))
+    cache = {}
+
+    def inputs(L):
+        if L not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cfg = DecodeWorkload(name="cal", description="", B=4, Hq=32, Hkv=8, L=L, d=128, Bc=64, lam=40.0 / L,
+                                 seed=11)
+            cache[L] = (cfg, gen_decode_inputs(cfg, device="cuda"))
+        return cache[L]
+
+    def measure(lam, L):
+        cfg, (q, kc, vc) = inputs(L)
+        return bsa.decode_sparsity(q, kc, vc, lam=lam, scale=cfg.scale)
+
+    log(f"calibration: target sparsity {target}, {len(lengths)} lengths x {len(lambdas)} thresholds")
+    a, n, table = bsa.calibrate(target, lengths, lambdas, delta, measure)
+    mid = len(lengths) // 2
+    row = np.abs(np.array(table[mid]) - target)
+    lam_fixed = float(lambdas[int(np.argmin(row))])
+    per = []
+    for k, L in enumerate(lengths):
+        best = int(np.argmin(np.abs(np.array(table[k]) - target)))
+        per.append({"L": L, "lambda_best": float(lambdas[best]), "sparsity_at_best": table[k][best],
+                    "sparsity_calibrated": measure(a / L, L) if n else None,
+                    "sparsity_fixed_lambda": measure(lam_fixed, L)})
+        log(f"calibration L {L}: calibrated {per[-1]['sparsity_calibrated']}, fixed {per[-1]['sparsity_fixed_lambda']}")
+    cache.clear()
+    torch.cuda.empty_cache()
+    return {"target": target, "delta": delta, "a": a, "n_points": n, "fixed_lambda": lam_fixed,
+            "recipe": "decode, B4 Hq32 Hkv8 d128, same generator as the 131K decode workload", "per_length": per}
+
+
 # ---------------------------------------------------------------------------- oracle on host cores
 
 def cpu_baseline_prefill(res, budget_s: float):
@@ -437,7 +483,9 @@ def main(argv=None) -> int:
             fn = sweep_decode if name == "cfg5" else sweep_prefill
             rep.append(fn(name, lams, min(a.steps, 50) if name != "cfg2" else a.steps, min(a.warmup, 20)
                           if name != "cfg2" else a.warmup))
-        print(json.dumps({"sweep": rep, "steps": a.steps, "device": torch.cuda.get_device_name(0)}))
+        cal = calibration_demo()
+        print(json.dumps({"sweep": rep, "calibration": cal, "steps": a.steps,
+                          "device": torch.cuda.get_device_name(0)}))
         return 0
     if a.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``prefill_workspace_size(B, Hq, d, n_slots)``, ``prefill_workspace(...)`` (zero-filled)
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
+* ``calibrate_fit(...)``, ``calibrate(target, lengths, lambdas, delta, measure)``,
+  ``decode_sparsity(...)``: threshold calibration lambda = a / L
 * ``prefill_plan(...)``, ``decode_plan(...)`` -> Plan: the same calls marshalled
   once; ``plan(stream=None)`` enqueues with a single C-ABI call
 * ``decode_workspace_size(...)``, ``decode_workspace(...)`` (zero-filled), ``decode_num_splits(...)``,
@@ -34,6 +36,7 @@ from . import _abi
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
     "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits", "decode_check",
+    "calibrate_fit", "calibrate", "decode_sparsity",
 ]
 
 
@@ -340,6 +343,42 @@ def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[
     ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None)."""
     return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
                        workspace=workspace, out=out, counters=counters, block_state=block_state)(stream)
+
+
+def calibrate_fit(target: float, lengths, lambdas, sparsity, delta: float):
+    """Algorithm 2's selection and fit on a measured table (C ABI):
+    sparsity[k][i] measured at lengths[k] with lambdas[i].  Returns (a, n_points)."""
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    lambdas = np.ascontiguousarray(lambdas, dtype=np.float64)
+    table = np.ascontiguousarray(sparsity, dtype=np.float64).reshape(lengths.size, lambdas.size)
+    a, n = C.c_double(0.0), C.c_int32(0)
+    _check(library().bsattn_calibrate_threshold(float(target), lengths.ctypes.data, lengths.size, lambdas.ctypes.data,
+                                                lambdas.size, table.ctypes.data, float(delta), C.byref(a),
+                                                C.byref(n)))
+    return float(a.value), int(n.value)
+
+
+def calibrate(target: float, lengths, lambdas, delta: float, measure):
+    """BLASST threshold calibration (notes section 3.2, Algorithm 2).
+
+    ``measure(lam, L)`` returns the sparsity measured at context length L with
+    threshold lam (for instance ``decode_sparsity`` on a sample of sequences
+    of that length).  Returns (a, n_points, table): lambda(L) = a / L."""
+    table = [[float(measure(lam, L)) for lam in lambdas] for L in lengths]
+    a, n = calibrate_fit(target, lengths, lambdas, table, delta)
+    return a, n, table
+
+
+def decode_sparsity(q, k_cache, v_cache, *, lam: float, L: Optional[int] = None, scale: Optional[float] = None,
+                    Bc: int = 64) -> float:
+    """Fraction of visited key blocks the decode kernel skips at threshold lam
+    (synchronous: reads the kernel's skip counters back)."""
+    torch = _torch()
+    B, Hkv = q.shape[0], k_cache.shape[2]
+    cnt = torch.zeros((B, Hkv, 2), dtype=torch.int32, device=q.device)
+    decode_fwd(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, counters=cnt)
+    c = cnt.view(-1, 2).sum(0).tolist()
+    return c[1] / c[0] if c[0] else 0.0
 
 
 def decode_check(workspace) -> int:

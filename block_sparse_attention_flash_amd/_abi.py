@@ -23,6 +23,7 @@ EXPORTED = (
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
     "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_fwd", "bsattn_decode_check",
+    "bsattn_calibrate_threshold",
 )
 
 
@@ -100,4 +101,7 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_decode_fwd.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
     lib.bsattn_decode_check.restype = C.c_int
     lib.bsattn_decode_check.argtypes = [C.c_void_p, C.POINTER(C.c_int32)]
+    lib.bsattn_calibrate_threshold.restype = C.c_int
+    lib.bsattn_calibrate_threshold.argtypes = [C.c_double, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                               C.c_double, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
     return lib

@@ -23,7 +23,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libbsattn.so")
 ARCH = os.environ.get("BSATTN_ARCH", "gfx950")
 
-HOST_SOURCES = ["api.cpp", "block_index.cpp"]
+HOST_SOURCES = ["api.cpp", "block_index.cpp", "calibrate.cpp"]
 DEVICE_SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
 
 

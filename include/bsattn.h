@@ -258,6 +258,24 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* args, void* stream);
  * valid. */
 bsattn_status bsattn_decode_check(void* workspace, int32_t* health_out);
 
+/* ------------------------------------------------------------------------ */
+/* threshold calibration (host only)                                          */
+/* ------------------------------------------------------------------------ */
+
+/* BLASST notes section 3.2 and Algorithm 2: the best threshold follows
+ * lambda = a / L.  For each context length lengths[k], the threshold of
+ * lambdas[] whose measured sparsity sparsity[k * n_lambdas + i] (fraction of
+ * visited blocks skipped, measured by the caller with the attention calls
+ * above) lies closest to `target` is kept when that distance is strictly
+ * below `delta` (the first of equal distances wins); *a_out is the slope of
+ * the least-squares line through the origin on the kept (1 / L, lambda)
+ * points and *n_points_out their number (0 leaves *a_out = NaN).
+ * Host buffers; target in [0, 1], delta > 0, lambdas in (0, 1), lengths >= 1,
+ * sparsities in [0, 1], else BSATTN_ERR_INVALID_ARG. */
+bsattn_status bsattn_calibrate_threshold(double target, const int32_t* lengths, int32_t n_lengths,
+                                         const double* lambdas, int32_t n_lambdas, const double* sparsity,
+                                         double delta, double* a_out, int32_t* n_points_out);
+
 #ifdef __cplusplus
 }
 #endif
