@@ -97,9 +97,12 @@ def tile_rows(t: int, Br: int, n_q: int) -> np.ndarray:
 
 
 def visited_blocks(t: int, Br: int, Bc: int, n_q: int, n_k: int, causal: bool,
-                   row_ptr=None, col_idx=None) -> np.ndarray:
-    """Key blocks visited by query tile t, ascending: the tile's CSR list (or
-    every block), minus blocks wholly above the diagonal when causal."""
+                   row_ptr=None, col_idx=None, order: str = "ascending") -> np.ndarray:
+    """Key blocks visited by query tile t: the tile's CSR list (or every block),
+    minus blocks wholly above the diagonal when causal, in ascending order
+    (Algorithm 1) or descending order (most recent keys first: the block-row
+    reordering the BLASST notes study, which finds a running max closer to
+    the row's global maximum sooner)."""
     Tc = -(-n_k // Bc)
     if row_ptr is None:
         blocks = np.arange(Tc)
@@ -108,6 +111,10 @@ def visited_blocks(t: int, Br: int, Bc: int, n_q: int, n_k: int, causal: bool,
     if causal:
         last_row = min((t + 1) * Br, n_q) - 1
         blocks = blocks[blocks * Bc <= last_row]
+    if order == "descending":
+        blocks = blocks[::-1].copy()
+    elif order != "ascending":
+        raise ValueError(order)
     return blocks
 
 
@@ -254,7 +261,7 @@ def static_tile(qr, k, v, rows, blocks, Bc: int, scale: float, n_valid: int, cau
 
 def prefill_tile(q, k, v, b: int, h: int, t: int, *, Br: int, Bc: int, scale: float,
                  causal: bool, lam: float, n_valid: int, row_ptr=None, col_idx=None,
-                 force=None, method: str = "loop"):
+                 force=None, method: str = "loop", order: str = "ascending"):
     """Oracle output of one (batch, query head, query tile) of a prefill call.
 
     q [B, N, Hq, d], k/v [B, N, Hkv, d] (torch or numpy).  Returns
@@ -265,7 +272,7 @@ def prefill_tile(q, k, v, b: int, h: int, t: int, *, Br: int, Bc: int, scale: fl
     n_q, n_k = q.shape[1], k.shape[1]
     g = kv_head_of(h, Hq, Hkv)
     rows = tile_rows(t, Br, n_q)
-    blocks = visited_blocks(t, Br, Bc, n_q, n_k, causal, row_ptr, col_idx)
+    blocks = visited_blocks(t, Br, Bc, n_q, n_k, causal, row_ptr, col_idx, order)
     qr = as_f64(q[b, rows[0]:rows[-1] + 1, h])
     kk = as_f64(k[b, :, g])
     vv = as_f64(v[b, :, g])
@@ -282,21 +289,34 @@ def prefill_tile(q, k, v, b: int, h: int, t: int, *, Br: int, Bc: int, scale: fl
 # decode: one new query token per sequence, tile = the G heads of a K/V head
 # ---------------------------------------------------------------------------
 
-def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "loop", force=None):
+def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "loop", force=None,
+                 order: str = "ascending"):
     """Decode oracle for one (sequence, K/V head): qg [G, d] are the G query
     heads sharing the K/V head, kg/vg [L, d] its cache.  The query sits at
-    position L-1 and sees keys 0..L-1, visited in ascending blocks of Bc.
+    position L-1 and sees keys 0..L-1, visited in blocks of Bc in ascending
+    order, or descending (most recent first) with order="descending".
 
     "loop" runs Algorithm 1 literally; "closed_form" takes the skip set from
-    the cumulative-max form and then the masked softmax over kept keys."""
+    the cumulative-max form (running in the visiting order) and then the
+    masked softmax over kept keys.  skip, margin and ``force`` are indexed by
+    block number whatever the order."""
     qg, kg, vg = as_f64(qg), as_f64(kg), as_f64(vg)
     L = kg.shape[0]
     G = qg.shape[0]
     Tc = -(-L // Bc)
-    blocks = np.arange(Tc)
+    if order == "ascending":
+        blocks = np.arange(Tc)
+    elif order == "descending":
+        blocks = np.arange(Tc)[::-1].copy()
+    else:
+        raise ValueError(order)
     rows = np.full(G, L - 1)          # every head's query sits at position L-1
     if method == "loop":
-        out, skip, margin = blasst_tile(qg, kg, vg, rows, blocks, Bc, scale, lam, L, False, force)
+        fpos = None if force is None else {int(np.nonzero(blocks == j)[0][0]): v for j, v in force.items()}
+        out, skip_v, margin_v = blasst_tile(qg, kg, vg, rows, blocks, Bc, scale, lam, L, False, fpos)
+        skip = np.zeros(Tc, dtype=bool)
+        margin = np.zeros(Tc)
+        skip[blocks], margin[blocks] = skip_v, margin_v
         return out, skip, margin
     if method != "closed_form":
         raise ValueError(method)
@@ -304,9 +324,11 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     S = scale * (qg @ kg.T)                                   # [G, L]
     pad = np.full((G, Tc * Bc), -np.inf)
     pad[:, :L] = S
-    bm = pad.reshape(G, Tc, Bc).max(axis=2)                    # [G, Tc]
+    bm = pad.reshape(G, Tc, Bc).max(axis=2)[:, blocks]         # [G, Tc], visiting order
     cm = np.maximum.accumulate(bm, axis=1)
-    gap = bm - cm
+    gap_v = bm - cm
+    gap = np.empty_like(gap_v)
+    gap[:, blocks] = gap_v                                     # back to block order
     if lam == 0.0:
         skip = np.zeros(Tc, dtype=bool)
         margin = np.full(Tc, np.inf)
@@ -323,7 +345,7 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
 
 
 def decode_sequence(q, k, v, Bc: int, scale: float, lam: float, method: str = "closed_form",
-                    groups=None):
+                    groups=None, order: str = "ascending"):
     """Decode oracle for one sequence: q [Hq, d], k/v [L, Hkv, d].
     Returns out [Hq, d] (NaN for heads of groups not computed), skip [Hkv, Tc], margin [Hkv, Tc]."""
     Hq, d = q.shape
@@ -334,7 +356,7 @@ def decode_sequence(q, k, v, Bc: int, scale: float, lam: float, method: str = "c
     skip = np.zeros((Hkv, Tc), dtype=bool)
     margin = np.full((Hkv, Tc), np.nan)
     for g in (range(Hkv) if groups is None else groups):
-        o, s, mg = decode_group(q[g * G:(g + 1) * G], k[:, g], v[:, g], Bc, scale, lam, method)
+        o, s, mg = decode_group(q[g * G:(g + 1) * G], k[:, g], v[:, g], Bc, scale, lam, method, order=order)
         out[g * G:(g + 1) * G] = o
         skip[g], margin[g] = s, mg
     return out, skip, margin

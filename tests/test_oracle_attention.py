@@ -227,6 +227,62 @@ def test_row_agreement_brute_force_and_invariants(lam):
     assert A.row_agreement(qr, kk, rows, blocks, 32, 0.25, 0.0, 160, True)[0].sum() == 0
 
 
+def _block_const_keys(a, Bc=4):
+    """Keys whose scores against q = (1, 0) equal a[j] on every key of block j."""
+    k = np.zeros((len(a) * Bc, 2))
+    k[:, 0] = np.repeat(np.asarray(a, dtype=float), Bc)
+    v = np.repeat(np.arange(len(a), dtype=float) * 10.0 + 1.0, Bc)[:, None]
+    return np.array([[1.0, 0.0]]), k, v
+
+
+def test_descending_order_worked_example():
+    # block maxima 5, 0, 3, -2, 4, 1 and ln(lambda) = -2 (scale 1):
+    # ascending running max 5 everywhere -> gaps 0 -5 -2 -7 -1 -4 -> skip {1, 3, 5};
+    # descending visits 1, 4, -2, 3, 0, 5 with running max 1 4 4 4 4 5 -> gaps (by block)
+    # 0 -4 -1 -6 0 0 -> skip {1, 3}
+    a = [5.0, 0.0, 3.0, -2.0, 4.0, 1.0]
+    q, k, v = _block_const_keys(a)
+    lam = math.exp(-2.0)
+    for meth in ("loop", "closed_form"):
+        _, s_up, _ = A.decode_group(q, k, v, 4, 1.0, lam, meth)
+        _, s_dn, _ = A.decode_group(q, k, v, 4, 1.0, lam, meth, order="descending")
+        assert np.nonzero(s_up)[0].tolist() == [1, 3, 5], meth
+        assert np.nonzero(s_dn)[0].tolist() == [1, 3], meth
+
+
+def test_descending_order_mirror_symmetry_and_forms():
+    """Reversing the key blocks and visiting in descending order is ascending
+    order on the original blocks: the skip sets mirror.  The literal loop and
+    the closed form agree in descending order; at lambda = 0 the order does
+    not change the output."""
+    cfg = DecodeWorkload(name="o", description="", B=1, Hq=4, Hkv=1, L=64 * 24, d=32, Bc=64, lam=0.0, seed=31)
+    q, k, v = gen_decode_sequence(cfg, 0)
+    q, k, v = A.as_f64(q), A.as_f64(k)[:, 0], A.as_f64(v)[:, 0]
+    L, Bc = k.shape[0], 64
+    perm = np.concatenate([np.arange(j * Bc, (j + 1) * Bc) for j in range(L // Bc)[::-1]])
+    for lam in (1e-3, 0.02, 0.2):
+        _, s_up, _ = A.decode_group(q, k, v, Bc, cfg.scale, lam, "closed_form")
+        _, s_mir, _ = A.decode_group(q, k[perm], v[perm], Bc, cfg.scale, lam, "closed_form", order="descending")
+        assert np.array_equal(s_mir[::-1], s_up)
+        o_l, s_l, _ = A.decode_group(q, k, v, Bc, cfg.scale, lam, "loop", order="descending")
+        o_c, s_c, _ = A.decode_group(q, k, v, Bc, cfg.scale, lam, "closed_form", order="descending")
+        assert np.array_equal(s_l, s_c) and np.max(np.abs(o_l - o_c)) < 1e-12
+    o_up, _, _ = A.decode_group(q, k, v, Bc, cfg.scale, 0.0, "loop")
+    o_dn, _, _ = A.decode_group(q, k, v, Bc, cfg.scale, 0.0, "loop", order="descending")
+    assert np.max(np.abs(o_up - o_dn)) < 1e-12
+    # prefill tile, causal: descending visits the diagonal block first
+    pc, (qq, kk, vv) = _concentrated_case(L=256, Hq=2, Hkv=1, d=16)
+    blocks_dn = A.visited_blocks(3, 64, 32, 256, 256, True, order="descending")
+    assert blocks_dn.tolist() == list(range(7, -1, -1))
+    for lam in (0.05, 0.3):
+        _, _, b_dn, s_dn, _ = A.prefill_tile(qq, kk, vv, 0, 0, 3, Br=64, Bc=32, scale=0.25, causal=True, lam=lam,
+                                             n_valid=256, order="descending")
+        rows = A.tile_rows(3, 64, 256)
+        sv, _ = A.skip_set_vectorized(A.as_f64(qq[0, rows[0]:rows[-1] + 1, 0]), A.as_f64(kk[0, :, 0]), rows, b_dn,
+                                      32, 0.25, lam, 256, True)
+        assert np.array_equal(s_dn, sv)
+
+
 def test_skip_monotone_and_first_block_kept():
     cfg, (q, k, v) = _concentrated_case()
     prev = None
