@@ -198,6 +198,12 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _order_code(order: str) -> int:
+    if order not in ("ascending", "descending"):
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, f"order must be 'ascending' or 'descending', not {order!r}")
+    return 1 if order == "descending" else 0
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -220,7 +226,7 @@ class Plan:
 def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                  Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
                  out=None, tile_counters=None, block_state=None, row_counters=None,
-                 schedule: Optional[Schedule] = None, workspace=None) -> Plan:
+                 schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending") -> Plan:
     """Marshal a prefill (arguments as ``prefill_fwd``) into a reusable Plan."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
@@ -252,6 +258,7 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
     a.Br, a.Bc = int(Br), int(Bc)
     a.tile_counters, a.block_state = _ptr(tile_counters), _ptr(block_state)
     a.row_counters = _ptr(row_counters)
+    a.block_order = _order_code(order)
     if schedule is not None:
         if schedule.d_items is None:
             schedule.to(q.device)
@@ -269,20 +276,22 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
 def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                 Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
                 out=None, tile_counters=None, block_state=None, row_counters=None,
-                schedule: Optional[Schedule] = None, workspace=None, stream=None):
+                schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending", stream=None):
     """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
 
     ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
     ``tile_counters`` int32 [B, Hq, Tr, 2] and ``block_state`` uint8
     [B, Hq, Tr, Tc] are optional device outputs, as is ``row_counters`` int32
-    [B, Hq, Tr] (per-row skip conditions that held, for lambda > 0).  ``schedule`` (from
+    [B, Hq, Tr] (per-row skip conditions that held, for lambda > 0).
+    ``order`` "descending" visits each tile's blocks most recent first (the
+    BLASST notes' block-row reordering).  ``schedule`` (from
     ``build_schedule``, device copies made with ``.to``) cuts long tiles;
     its partials go to ``workspace`` (a uint8 device tensor from
     ``prefill_workspace``, allocated here if None).  Returns ``out``."""
     return prefill_plan(q, k, v, scale=scale, lam=lam, causal=causal, Br=Br, Bc=Bc, row_ptr=row_ptr,
                         col_idx=col_idx, tile_order=tile_order, n_valid=n_valid, out=out,
                         tile_counters=tile_counters, block_state=block_state, row_counters=row_counters,
-                        schedule=schedule,
+                        schedule=schedule, order=order,
                         workspace=workspace)(stream)
 
 
@@ -303,7 +312,7 @@ def decode_num_splits(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, n
 
 def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                 Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None,
-                block_state=None) -> Plan:
+                block_state=None, order: str = "ascending") -> Plan:
     """Marshal a decode (arguments as ``decode_fwd``) into a reusable Plan."""
     torch = _torch()
     B, Hq, d = q.shape
@@ -330,19 +339,21 @@ def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     a.counters, a.block_state = _ptr(counters), _ptr(block_state)
+    a.block_order = _order_code(order)
     keep = (q, k_cache, v_cache, workspace, counters, block_state)
     return Plan(library().bsattn_decode_fwd, a, out, keep)
 
 
 def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
-               stream=None):
+               order: str = "ascending", stream=None):
     """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
 
     ``workspace`` is a uint8 device tensor of at least
     ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None)."""
     return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
-                       workspace=workspace, out=out, counters=counters, block_state=block_state)(stream)
+                       workspace=workspace, out=out, counters=counters, block_state=block_state,
+                       order=order)(stream)
 
 
 def calibrate_fit(target: float, lengths, lambdas, sparsity, delta: float):
@@ -370,13 +381,13 @@ def calibrate(target: float, lengths, lambdas, delta: float, measure):
 
 
 def decode_sparsity(q, k_cache, v_cache, *, lam: float, L: Optional[int] = None, scale: Optional[float] = None,
-                    Bc: int = 64) -> float:
+                    Bc: int = 64, order: str = "ascending") -> float:
     """Fraction of visited key blocks the decode kernel skips at threshold lam
     (synchronous: reads the kernel's skip counters back)."""
     torch = _torch()
     B, Hkv = q.shape[0], k_cache.shape[2]
     cnt = torch.zeros((B, Hkv, 2), dtype=torch.int32, device=q.device)
-    decode_fwd(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, counters=cnt)
+    decode_fwd(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, counters=cnt, order=order)
     c = cnt.view(-1, 2).sum(0).tolist()
     return c[1] / c[0] if c[0] else 0.0
 

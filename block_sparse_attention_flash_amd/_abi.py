@@ -50,6 +50,7 @@ class PrefillArgs(C.Structure):
                 ("Br", C.c_int32), ("Bc", C.c_int32),
                 ("tile_counters", C.c_void_p), ("block_state", C.c_void_p),
                 ("row_counters", C.c_void_p),
+                ("block_order", C.c_int32),
                 ("sched_items", C.c_void_p), ("n_items", C.c_int32), ("sched_merges", C.c_void_p),
                 ("n_merges", C.c_int32), ("n_slots", C.c_int32), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t)]
@@ -62,7 +63,7 @@ class DecodeArgs(C.Structure):
                 ("q_stride", C.c_int64 * 2), ("kv_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 2),
                 ("scale", C.c_float), ("lam", C.c_float), ("Bc", C.c_int32), ("num_splits", C.c_int32),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("counters", C.c_void_p), ("block_state", C.c_void_p)]
+                ("counters", C.c_void_p), ("block_state", C.c_void_p), ("block_order", C.c_int32)]
 
 
 def load(path: str = None) -> C.CDLL:

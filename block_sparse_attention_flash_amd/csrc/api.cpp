@@ -173,6 +173,8 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   p.Tc = (a->Nk + a->Bc - 1) / a->Bc;
   p.tile_counters = a->tile_counters; p.block_state = a->block_state;
   p.row_counters = a->row_counters;
+  if (a->block_order != 0 && a->block_order != 1) return fail(BSATTN_ERR_INVALID_ARG, "block_order must be 0 or 1");
+  p.block_order = a->block_order;
   if (a->sched_items) {
     if (a->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "schedules are implemented for the bf16 path");
     if (!a->row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a schedule needs the CSR (row_ptr, col_idx)");
@@ -257,11 +259,13 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   p.scale = a->scale; p.lambda = a->lambda; p.Bc = a->Bc;
   p.Tc = (a->L + a->Bc - 1) / a->Bc;
   p.num_splits = decode_choose_splits(a->B, a->Hkv, p.Tc, G, a->num_splits, &p.blocks_per_split);
+  if (a->block_order != 0 && a->block_order != 1) return fail(BSATTN_ERR_INVALID_ARG, "block_order must be 0 or 1");
   const DecodeWorkspace w = decode_workspace_layout(a->B, a->Hq, a->Hkv, a->d, p.num_splits);
   if (a->workspace_bytes < w.total)
     return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
   if ((int64_t)a->B * a->Hkv * p.num_splits > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   p.workspace = a->workspace; p.counters = a->counters; p.block_state = a->block_state;
+  p.block_order = a->block_order;
   return hip_status(launch_decode(p, stream), "decode launch");
 }
 

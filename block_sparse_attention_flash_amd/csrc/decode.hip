@@ -138,8 +138,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   const int s = sm.ticket;
   const int b = pair / p.Hkv, g = pair % p.Hkv;
   const int unit = pair * S + s;
-  const int blk0 = s * p.blocks_per_split;
-  const int nb = min(p.blocks_per_split, p.Tc - blk0);
+  // split s in visiting order: ascending, its blocks are [s bps, (s+1) bps);
+  // descending (most recent keys first), split 0 holds the last blocks
+  const int desc = p.block_order;
+  const int blk0 = desc ? max(0, p.Tc - (s + 1) * p.blocks_per_split) : s * p.blocks_per_split;
+  const int nb = desc ? p.Tc - s * p.blocks_per_split - blk0 : min(p.blocks_per_split, p.Tc - blk0);
   const float c2 = p.scale * kLog2e;
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b;
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
     if (lane < G) {
       float cm = sm.pre[lane];
       agree = 0ull;
-      for (int lb = 0; lb < nb; ++lb) {
+      for (int v = 0; v < nb; ++v) {  // the running max in visiting order
+        const int lb = desc ? nb - 1 - v : v;
         const float x = sm.bm[lb][lane];
         cm = fmaxf(cm, x);
         if (x == kNegInf || x - cm < log2_lambda) agree |= (1ull << lb);

@@ -39,6 +39,7 @@ struct PrefillParams {
   int32_t* tile_counters;
   uint8_t* block_state;
   int32_t* row_counters;
+  int32_t block_order;
   const int32_t* sched_items;   // [n_items][5] or NULL
   int32_t n_items;
   const int32_t* sched_merges;  // [n_merges][3]
@@ -74,6 +75,7 @@ struct DecodeParams {
   void* workspace;
   int32_t* counters;
   uint8_t* block_state;
+  int32_t block_order;
 };
 
 // Decode workspace layout (all offsets 256-byte aligned), see decode.hip.

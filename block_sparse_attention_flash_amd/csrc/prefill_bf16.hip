@@ -316,7 +316,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   // they never share the vector-memory counter with the K/V loads
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const const_i32_ptr ccols = cols ? (const_i32_ptr)(cols) : nullptr;
-  auto blk = [&](int i) __attribute__((always_inline)) { return i < nblk ? (ccols ? ccols[i] : e0 + i) : 0; };
+  // visiting position i -> key block: ascending, or descending (most recent keys first)
+  const bool desc = p.block_order != 0;
+  auto blk = [&](int i) __attribute__((always_inline)) {
+    const int e = desc ? nblk - 1 - i : i;
+    return i < nblk ? (ccols ? ccols[e] : e0 + e) : 0;
+  };
   TileSrc<D, false> ksrc;
   TileSrc<D, true> vsrc;
   ksrc.init(kbase, p.ks_t, p.Nk, wave, lane);

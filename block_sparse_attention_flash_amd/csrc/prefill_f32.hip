@@ -53,10 +53,15 @@ __global__ __launch_bounds__(BR) void prefill_f32_kernel(const PrefillParams p) 
     beg = p.row_ptr[t];
     end = p.row_ptr[t + 1];
   }
+  if (p.causal) {  // ascending list: drop the entries wholly above the diagonal
+    int n = beg;
+    while (n < end && (p.row_ptr ? p.col_idx[n] : n) * BC <= last_row) ++n;
+    end = n;
+  }
   int visited = 0, skipped = 0, rows_agree = 0;
-  for (int e = beg; e < end; ++e) {
+  for (int it = 0; it < end - beg; ++it) {
+    const int e = p.block_order ? end - 1 - it : beg + it;  // descending: most recent keys first
     const int j = p.row_ptr ? p.col_idx[e] : e;
-    if (p.causal && j * BC > last_row) break;  // ascending: nothing further is visited
     ++visited;
     // stage K block
     __syncthreads();

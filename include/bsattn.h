@@ -184,6 +184,9 @@ typedef struct {
                              before the tile-wide vote (BLASST notes sections 3.1.1 and 4);
                              0 for lambda = 0.  Compare with skipped x rows for the cost of
                              tile-wide decisions */
+  int32_t block_order;    /* 0: visited blocks in ascending order (Algorithm 1); 1: descending,
+                             most recent keys first (the block-row reordering the BLASST notes
+                             study).  The order changes which blocks lambda > 0 skips */
   const int32_t* sched_items;  /* optional device copy of bsattn_build_schedule's items (needs the CSR);
                                   NULL = one work-group per tile (tile_order applies) */
   int32_t n_items;
@@ -238,6 +241,8 @@ typedef struct {
   size_t workspace_bytes;
   int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks */
   uint8_t* block_state;   /* optional device [B, Hkv, Tc]: 1 computed, 2 skipped */
+  int32_t block_order;    /* 0: ascending key blocks (Algorithm 1); 1: descending, most recent
+                             keys first (block-row reordering, BLASST notes) */
 } bsattn_decode_args;
 
 /* Workspace bytes for a decode call with these sizes (num_splits as in the args). */

@@ -33,7 +33,8 @@ def compare_out(got, ref, fp32: bool, what: str):
 
 
 def check_prefill_tile(q, k, v, out_gpu, state_gpu, counters_gpu, b, h, t, *, Br, Bc, scale, causal, lam,
-                       n_valid, row_ptr=None, col_idx=None, fp32=False, rows_limit=None, method="loop"):
+                       n_valid, row_ptr=None, col_idx=None, fp32=False, rows_limit=None, method="loop",
+                       order="ascending"):
     """Oracle for one (b, h, t); compares visited set, skip set, counters and the output rows.
 
     q/k/v/out_gpu/state_gpu/counters_gpu are host tensors or arrays.  Returns
@@ -41,7 +42,7 @@ def check_prefill_tile(q, k, v, out_gpu, state_gpu, counters_gpu, b, h, t, *, Br
     Tc = -(-k.shape[1] // Bc)
     rows, ref, blocks, skip, margin = A.prefill_tile(q, k, v, b, h, t, Br=Br, Bc=Bc, scale=scale, causal=causal,
                                                      lam=lam, n_valid=n_valid, row_ptr=row_ptr, col_idx=col_idx,
-                                                     method=method)
+                                                     method=method, order=order)
     st = np.asarray(state_gpu[b, h, t])
     visited = np.zeros(Tc, bool)
     visited[blocks] = True

@@ -33,7 +33,7 @@ def _shared_workspace(nbytes):
     return _WS[0]
 
 
-def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None):
+def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None, order="ascending"):
     B, Hq, d = q.shape
     Hkv = kc.shape[2]
     L = kc.shape[1] if L is None else L
@@ -42,18 +42,18 @@ def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None):
     state = torch.zeros((B, Hkv, Tc), dtype=torch.uint8, device=DEV)
     counters = torch.full((B, Hkv, 2), -1, dtype=torch.int32, device=DEV)
     out = bsa.decode_fwd(q, kc, vc, L=L, scale=cfg.scale, lam=cfg.lam if lam is None else lam,
-                         num_splits=num_splits, workspace=ws, counters=counters, block_state=state)
+                         num_splits=num_splits, workspace=ws, counters=counters, block_state=state, order=order)
     torch.cuda.synchronize()
     assert bsa.decode_check(ws) == 0, "decode look-back wait timed out"
     return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
 
 
-def check_sequence(q, k, v, out, st, cnt, b, L, scale, lam, groups=None):
+def check_sequence(q, k, v, out, st, cnt, b, L, scale, lam, groups=None, order="ascending"):
     """q [Hq, d], k/v [L, Hkv, d] host copies of sequence b."""
     Hq = q.shape[0]
     Hkv = k.shape[1]
     G = Hq // Hkv
-    ref, skip, margin = A.decode_sequence(q, k[:L], v[:L], 64, scale, lam, "closed_form", groups=groups)
+    ref, skip, margin = A.decode_sequence(q, k[:L], v[:L], 64, scale, lam, "closed_form", groups=groups, order=order)
     tot = [0, 0]
     for g in (range(Hkv) if groups is None else groups):
         gs = st[b, g] == 2
@@ -64,7 +64,8 @@ def check_sequence(q, k, v, out, st, cnt, b, L, scale, lam, groups=None):
         r = ref[g * G:(g + 1) * G]
         if ((gs != skip[g]) & excused).any():
             force = {int(i): bool(gs[i]) for i in np.nonzero((gs != skip[g]) & excused)[0]}
-            r, _, _ = A.decode_group(q[g * G:(g + 1) * G], k[:L, g], v[:L, g], 64, scale, lam, "closed_form", force)
+            r, _, _ = A.decode_group(q[g * G:(g + 1) * G], k[:L, g], v[:L, g], 64, scale, lam, "closed_form", force,
+                                     order=order)
         assert cnt[b, g, 0] == st.shape[2] and cnt[b, g, 1] == int(gs.sum())
         compare_out(A.as_f64(out[b, g * G:(g + 1) * G]), r, False, f"decode b{b} g{g}")
         tot[0] += gs.size
@@ -151,3 +152,24 @@ def test_decode_plan_and_graph_replays():
         assert torch.equal(plan.out, ref), r
         assert bsa.decode_check(ws) == 0
     del junk
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 7])
+def test_decode_descending_order(num_splits):
+    """Most recent blocks first (block-row reordering): skip sets and outputs
+    against the oracle in descending order, for several split counts (the
+    look-back then runs from the end of the sequence)."""
+    L = 5000
+    cfg = DecodeWorkload(name="s", description="", B=2, Hq=8, Hkv=2, L=L, d=128, Bc=64, lam=40.0 / L, seed=27)
+    _say(f"decode descending order, {num_splits} splits")
+    q, kc, vc = gen_decode_inputs(cfg)
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    tot = [0, 0]
+    for lam in (0.3, 0.5):       # the sink block is visited last: smaller thresholds skip nothing here
+        out, st, cnt = run_decode(cfg, qd, kd, vd, num_splits=num_splits, lam=lam, order="descending")
+        for b in range(cfg.B):
+            r = check_sequence(q[b], kc[b], vc[b], out, st, cnt, b, L, cfg.scale, lam, order="descending")
+            tot = [x + y for x, y in zip(tot, r)]
+    asc = run_decode(cfg, qd, kd, vd, num_splits=num_splits, lam=0.3)
+    _say(f"  skipped {tot[1]} of {tot[0]} (descending), {int(asc[2][..., 1].sum())} ascending at lambda 0.3")
+    assert tot[1] > 0

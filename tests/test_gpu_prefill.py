@@ -23,7 +23,8 @@ def _say(msg):
     print(f"[gpu-prefill] {msg}", file=sys.stderr, flush=True)
 
 
-def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedule=None, workspace=None):
+def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedule=None, workspace=None,
+                block_order="ascending"):
     """Launch through the binding; returns host copies of out, block_state, counters."""
     Br = cfg.Br if Br is None else Br
     B, N, Hq, d = q.shape
@@ -38,7 +39,8 @@ def run_prefill(cfg, q, k, v, *, csr=None, order=None, lam=None, Br=None, schedu
         od = torch.from_numpy(order).to(DEV)
     out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, lam=cfg.lam if lam is None else lam, causal=cfg.causal,
                           Br=Br, Bc=cfg.Bc, row_ptr=rp, col_idx=ci, tile_order=od, n_valid=cfg.n_valid,
-                          tile_counters=counters, block_state=state, schedule=schedule, workspace=workspace)
+                          tile_counters=counters, block_state=state, schedule=schedule, workspace=workspace,
+                          order=block_order)
     torch.cuda.synchronize()
     return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
 
@@ -340,3 +342,29 @@ def test_row_counters_match_oracle(dtype, d):
                     col_idx=ci, n_valid=spec.n_valid, row_counters=rc0)
     torch.cuda.synchronize()
     assert int(rc0.cpu().abs().sum()) == 0
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("fp32", 64)])
+def test_descending_block_order(dtype, d):
+    """Blocks of each tile visited most recent first: causal dynamic and static
+    CSR plus dynamic, skip sets and outputs against the oracle in that order."""
+    Br = 128 if dtype == "bf16" else 64
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid
+    for lam, causal, csr_on, gen in ((0.3, True, False, "sink"), (0.05, True, True, "concentrated"),
+                                     (0.6, False, True, "sink")):
+        cfg = _small("desc", dtype=dtype, N=n, d=d, Hq=4, Hkv=2, causal=causal, lam=lam, generator=gen, seed=14)
+        _say(f"descending order {dtype} d{d} lambda {lam} causal={causal} csr={csr_on}")
+        q, k, v = gen_prefill_inputs(cfg)
+        csr = bsa.build_block_index(spec, n, n, Br, 64) if csr_on else None
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, Br=Br, block_order="descending")
+        tot = [0, 0, 0]
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                for t in range(-(-n // Br)):
+                    r = check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=Br, Bc=64, scale=cfg.scale,
+                                           causal=causal, lam=lam, n_valid=n, fp32=dtype == "fp32",
+                                           row_ptr=None if csr is None else csr[0],
+                                           col_idx=None if csr is None else csr[1], order="descending")
+                    tot = [x + y for x, y in zip(tot, r)]
+        _say(f"  visited {tot[0]} skipped {tot[1]} excused {tot[2]}")
