@@ -290,7 +290,7 @@ def prefill_tile(q, k, v, b: int, h: int, t: int, *, Br: int, Bc: int, scale: fl
 # ---------------------------------------------------------------------------
 
 def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "loop", force=None,
-                 order: str = "ascending"):
+                 order: str = "ascending", split_blocks: int = 0):
     """Decode oracle for one (sequence, K/V head): qg [G, d] are the G query
     heads sharing the K/V head, kg/vg [L, d] its cache.  The query sits at
     position L-1 and sees keys 0..L-1, visited in blocks of Bc in ascending
@@ -299,7 +299,12 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     "loop" runs Algorithm 1 literally; "closed_form" takes the skip set from
     the cumulative-max form (running in the visiting order) and then the
     masked softmax over kept keys.  skip, margin and ``force`` are indexed by
-    block number whatever the order."""
+    block number whatever the order.
+
+    ``split_blocks`` > 0 selects the per-split variant (not the pages'
+    method; it quantifies what the exact cross-split prefix buys): the
+    visiting sequence is cut into runs of split_blocks blocks and the running
+    max restarts at -inf at the start of every run."""
     qg, kg, vg = as_f64(qg), as_f64(kg), as_f64(vg)
     L = kg.shape[0]
     G = qg.shape[0]
@@ -312,6 +317,8 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
         raise ValueError(order)
     rows = np.full(G, L - 1)          # every head's query sits at position L-1
     if method == "loop":
+        if split_blocks:
+            raise ValueError("the per-split variant has the closed form only")
         fpos = None if force is None else {int(np.nonzero(blocks == j)[0][0]): v for j, v in force.items()}
         out, skip_v, margin_v = blasst_tile(qg, kg, vg, rows, blocks, Bc, scale, lam, L, False, fpos)
         skip = np.zeros(Tc, dtype=bool)
@@ -325,7 +332,11 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     pad = np.full((G, Tc * Bc), -np.inf)
     pad[:, :L] = S
     bm = pad.reshape(G, Tc, Bc).max(axis=2)[:, blocks]         # [G, Tc], visiting order
-    cm = np.maximum.accumulate(bm, axis=1)
+    if split_blocks:
+        cm = np.concatenate([np.maximum.accumulate(bm[:, a:a + split_blocks], axis=1)
+                             for a in range(0, Tc, split_blocks)], axis=1)
+    else:
+        cm = np.maximum.accumulate(bm, axis=1)
     gap_v = bm - cm
     gap = np.empty_like(gap_v)
     gap[:, blocks] = gap_v                                     # back to block order
@@ -345,7 +356,7 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
 
 
 def decode_sequence(q, k, v, Bc: int, scale: float, lam: float, method: str = "closed_form",
-                    groups=None, order: str = "ascending"):
+                    groups=None, order: str = "ascending", split_blocks: int = 0):
     """Decode oracle for one sequence: q [Hq, d], k/v [L, Hkv, d].
     Returns out [Hq, d] (NaN for heads of groups not computed), skip [Hkv, Tc], margin [Hkv, Tc]."""
     Hq, d = q.shape
@@ -356,7 +367,8 @@ def decode_sequence(q, k, v, Bc: int, scale: float, lam: float, method: str = "c
     skip = np.zeros((Hkv, Tc), dtype=bool)
     margin = np.full((Hkv, Tc), np.nan)
     for g in (range(Hkv) if groups is None else groups):
-        o, s, mg = decode_group(q[g * G:(g + 1) * G], k[:, g], v[:, g], Bc, scale, lam, method, order=order)
+        o, s, mg = decode_group(q[g * G:(g + 1) * G], k[:, g], v[:, g], Bc, scale, lam, method, order=order,
+                                split_blocks=split_blocks)
         out[g * G:(g + 1) * G] = o
         skip[g], margin[g] = s, mg
     return out, skip, margin

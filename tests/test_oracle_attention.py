@@ -283,6 +283,32 @@ def test_descending_order_mirror_symmetry_and_forms():
         assert np.array_equal(s_dn, sv)
 
 
+def test_per_split_reset_variant():
+    """The per-split variant restarts the running max at every split: worked
+    example by hand, equal to the exact rule when one split holds all blocks,
+    and equal to running each split as its own sequence."""
+    a = [5.0, 0.0, 3.0, -2.0, 4.0, 1.0]
+    q, k, v = _block_const_keys(a)
+    lam = math.exp(-2.0)
+    # splits of 2 blocks: (5, 0) (3, -2) (4, 1) -> gaps 0 -5 | 0 -5 | 0 -3 -> skip {1, 3, 5}
+    _, s2, _ = A.decode_group(q, k, v, 4, 1.0, lam, "closed_form", split_blocks=2)
+    assert np.nonzero(s2)[0].tolist() == [1, 3, 5]
+    # splits of 3 blocks: (5, 0, 3) (-2, 4, 1) -> gaps 0 -5 -2 | 0 0 -3 -> skip {1, 5}
+    _, s3, _ = A.decode_group(q, k, v, 4, 1.0, lam, "closed_form", split_blocks=3)
+    assert np.nonzero(s3)[0].tolist() == [1, 5]
+    cfg = DecodeWorkload(name="o", description="", B=1, Hq=4, Hkv=1, L=64 * 20, d=32, Bc=64, lam=0.0, seed=33)
+    qq, kk, vv = gen_decode_sequence(cfg, 0)
+    qq, kk, vv = A.as_f64(qq), A.as_f64(kk)[:, 0], A.as_f64(vv)[:, 0]
+    for lam in (1e-3, 0.05):
+        _, exact, _ = A.decode_group(qq, kk, vv, 64, cfg.scale, lam, "closed_form")
+        _, whole, _ = A.decode_group(qq, kk, vv, 64, cfg.scale, lam, "closed_form", split_blocks=20)
+        assert np.array_equal(exact, whole)
+        _, per, _ = A.decode_group(qq, kk, vv, 64, cfg.scale, lam, "closed_form", split_blocks=8)
+        parts = [A.decode_group(qq, kk[a * 64:(a + 8) * 64], vv[a * 64:(a + 8) * 64], 64, cfg.scale, lam,
+                                "closed_form")[1] for a in (0, 8, 16)]
+        assert np.array_equal(per, np.concatenate(parts))
+
+
 def test_skip_monotone_and_first_block_kept():
     cfg, (q, k, v) = _concentrated_case()
     prev = None
