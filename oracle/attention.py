@@ -290,7 +290,7 @@ def prefill_tile(q, k, v, b: int, h: int, t: int, *, Br: int, Bc: int, scale: fl
 # ---------------------------------------------------------------------------
 
 def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "loop", force=None,
-                 order: str = "ascending", split_blocks: int = 0):
+                 order: str = "ascending", split_blocks: int = 0, decisions: str = "group"):
     """Decode oracle for one (sequence, K/V head): qg [G, d] are the G query
     heads sharing the K/V head, kg/vg [L, d] its cache.  The query sits at
     position L-1 and sees keys 0..L-1, visited in blocks of Bc in ascending
@@ -304,7 +304,14 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     ``split_blocks`` > 0 selects the per-split variant (not the pages'
     method; it quantifies what the exact cross-split prefix buys): the
     visiting sequence is cut into runs of split_blocks blocks and the running
-    max restarts at -inf at the start of every run."""
+    max restarts at -inf at the start of every run.
+
+    ``decisions="head"`` selects the per-head variant (not the pages' method,
+    whose tile is the group): every query head takes its own skip decisions,
+    as a tile of one row would.  skip and margin are then [G, Tc] and
+    ``force`` maps (head, block) pairs."""
+    if decisions not in ("group", "head"):
+        raise ValueError(decisions)
     qg, kg, vg = as_f64(qg), as_f64(kg), as_f64(vg)
     L = kg.shape[0]
     G = qg.shape[0]
@@ -319,6 +326,15 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     if method == "loop":
         if split_blocks:
             raise ValueError("the per-split variant has the closed form only")
+        if decisions == "head":        # one tile of one row per head
+            outs, skips, margins = [], [], []
+            for r in range(G):
+                fr = None if force is None else {j: v for (h, j), v in force.items() if h == r}
+                o, sk, mg = decode_group(qg[r:r + 1], kg, vg, Bc, scale, lam, "loop", fr or None, order)
+                outs.append(o[0])
+                skips.append(sk)
+                margins.append(mg)
+            return np.stack(outs), np.stack(skips), np.stack(margins)
         fpos = None if force is None else {int(np.nonzero(blocks == j)[0][0]): v for j, v in force.items()}
         out, skip_v, margin_v = blasst_tile(qg, kg, vg, rows, blocks, Bc, scale, lam, L, False, fpos)
         skip = np.zeros(Tc, dtype=bool)
@@ -340,6 +356,18 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
     gap_v = bm - cm
     gap = np.empty_like(gap_v)
     gap[:, blocks] = gap_v                                     # back to block order
+    if decisions == "head":
+        if lam == 0.0:
+            skip = np.zeros((G, Tc), dtype=bool)
+            margin = np.full((G, Tc), np.inf)
+        else:
+            skip = gap < lnl
+            margin = gap - lnl
+        if force is not None:
+            for (h, j), s in force.items():
+                skip[h, j] = bool(s)
+        allowed = np.repeat(~skip, Bc, axis=1)[:, :L]
+        return masked_attention(qg, kg, vg, allowed, scale), skip, margin
     if lam == 0.0:
         skip = np.zeros(Tc, dtype=bool)
         margin = np.full(Tc, np.inf)
@@ -356,21 +384,24 @@ def decode_group(qg, kg, vg, Bc: int, scale: float, lam: float, method: str = "l
 
 
 def decode_sequence(q, k, v, Bc: int, scale: float, lam: float, method: str = "closed_form",
-                    groups=None, order: str = "ascending", split_blocks: int = 0):
+                    groups=None, order: str = "ascending", split_blocks: int = 0, decisions: str = "group"):
     """Decode oracle for one sequence: q [Hq, d], k/v [L, Hkv, d].
-    Returns out [Hq, d] (NaN for heads of groups not computed), skip [Hkv, Tc], margin [Hkv, Tc]."""
+    Returns out [Hq, d] (NaN for heads of groups not computed), skip and
+    margin [Hkv, Tc] (per head, decisions="head": [Hq, Tc])."""
     Hq, d = q.shape
     L, Hkv, _ = k.shape
     G = Hq // Hkv
     Tc = -(-L // Bc)
+    nd = Hq if decisions == "head" else Hkv
+    per = G if decisions == "head" else 1
     out = np.full((Hq, v.shape[2]), np.nan)
-    skip = np.zeros((Hkv, Tc), dtype=bool)
-    margin = np.full((Hkv, Tc), np.nan)
+    skip = np.zeros((nd, Tc), dtype=bool)
+    margin = np.full((nd, Tc), np.nan)
     for g in (range(Hkv) if groups is None else groups):
         o, s, mg = decode_group(q[g * G:(g + 1) * G], k[:, g], v[:, g], Bc, scale, lam, method, order=order,
-                                split_blocks=split_blocks)
+                                split_blocks=split_blocks, decisions=decisions)
         out[g * G:(g + 1) * G] = o
-        skip[g], margin[g] = s, mg
+        skip[g * per:(g + 1) * per], margin[g * per:(g + 1) * per] = s, mg
     return out, skip, margin
 
 

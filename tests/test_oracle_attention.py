@@ -309,6 +309,48 @@ def test_per_split_reset_variant():
         assert np.array_equal(per, np.concatenate(parts))
 
 
+def test_per_head_decision_variant():
+    """Per-head decisions: the loop (a tile of one row per head) equals the
+    closed form; the group's skip set is the intersection of the heads' skip
+    sets (same running max per row, the vote only ANDs); with one head per
+    group the two variants coincide; a hand-built case where heads differ."""
+    cfg = DecodeWorkload(name="o", description="", B=1, Hq=8, Hkv=2, L=64 * 9 + 17, d=32, Bc=64, lam=0.0, seed=41)
+    q, k, v = gen_decode_sequence(cfg, 0)
+    for lam in (1e-3, 0.02, 0.2):
+        for order in ("ascending", "descending"):
+            o1, s1, m1 = A.decode_sequence(q, k, v, 64, cfg.scale, lam, "loop", order=order, decisions="head")
+            o2, s2, m2 = A.decode_sequence(q, k, v, 64, cfg.scale, lam, "closed_form", order=order,
+                                           decisions="head")
+            assert s1.shape == (8, 10)
+            assert np.array_equal(s1, s2)
+            assert np.allclose(m1, m2, atol=1e-12) and np.allclose(o1, o2, atol=1e-12)
+            _, sg, _ = A.decode_sequence(q, k, v, 64, cfg.scale, lam, "closed_form", order=order)
+            assert np.array_equal(sg, s2.reshape(2, 4, 10).all(axis=1))
+    # G = 1: a head is its group
+    q1, k1, v1 = q[:2], k, v
+    og, sg, _ = A.decode_sequence(q1, k1, v1, 64, cfg.scale, 0.05, "closed_form")
+    oh, sh, _ = A.decode_sequence(q1, k1, v1, 64, cfg.scale, 0.05, "closed_form", decisions="head")
+    assert np.array_equal(sg, sh) and np.allclose(og, oh, atol=1e-14)
+    # two heads, keys with block-constant scores: head 0 sees (5, 0, 3), head 1 sees (0, 5, 3);
+    # at ln(lambda) = -2 head 0 skips block 1 only, head 1 skips nothing, the group skips nothing
+    qh = np.zeros((2, 2))
+    qh[0, 0] = qh[1, 1] = 1.0
+    kh = np.zeros((12, 2))
+    for j, (a0, a1) in enumerate([(5.0, 0.0), (0.0, 5.0), (3.0, 3.0)]):
+        kh[4 * j:4 * j + 4] = (a0, a1)
+    vh = np.arange(24, dtype=np.float64).reshape(12, 2)
+    lam = math.exp(-2.0)
+    oh, sh, mh = A.decode_group(qh, kh, vh, 4, 1.0, lam, "closed_form", decisions="head")
+    assert sh.tolist() == [[False, True, False], [False, False, False]]
+    assert np.allclose(mh, [[2.0, -3.0, 0.0], [2.0, 2.0, 0.0]])
+    _, sgrp, _ = A.decode_group(qh, kh, vh, 4, 1.0, lam, "closed_form")
+    assert sgrp.tolist() == [False, False, False]
+    # head 0 attends to blocks 0 and 2 only: weights e^5 (4 keys) and e^3 (4 keys)
+    w0, w2 = math.exp(5.0), math.exp(3.0)
+    want0 = (w0 * vh[0:4].sum(0) + w2 * vh[8:12].sum(0)) / (4 * w0 + 4 * w2)
+    assert np.allclose(oh[0], want0, atol=1e-12)
+
+
 def test_skip_monotone_and_first_block_kept():
     cfg, (q, k, v) = _concentrated_case()
     prev = None
