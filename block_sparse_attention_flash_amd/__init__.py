@@ -19,7 +19,7 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
   ``decode_sparsity(...)``: threshold calibration lambda = a / L
 * ``prefill_plan(...)``, ``decode_plan(...)`` -> Plan: the same calls marshalled
   once; ``plan(stream=None)`` enqueues with a single C-ABI call
-* ``decode_workspace_size(...)``, ``decode_workspace(...)`` (zero-filled), ``decode_num_splits(...)``,
+* ``decode_workspace_size(...)``, ``decode_workspace(...)`` (zero-filled), ``decode_num_splits(...)``, ``decode_split_blocks(...)``,
   ``decode_check(workspace)`` (reads and clears the health word)
 """
 
@@ -35,7 +35,7 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
-    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits", "decode_check",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits", "decode_split_blocks", "decode_check",
     "calibrate_fit", "calibrate", "decode_sparsity",
 ]
 
@@ -204,6 +204,12 @@ def _order_code(order: str) -> int:
     return 1 if order == "descending" else 0
 
 
+def _choice_code(name: str, value: str, choices) -> int:
+    if value not in choices:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, f"{name} must be one of {choices}, not {value!r}")
+    return choices.index(value)
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -310,9 +316,15 @@ def decode_num_splits(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, n
     return int(library().bsattn_decode_num_splits(B, Hq, Hkv, L, d, Bc, num_splits))
 
 
+def decode_split_blocks(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:
+    """Key blocks per split (visiting positions [s n, (s + 1) n) form split s)."""
+    return int(library().bsattn_decode_split_blocks(B, Hq, Hkv, L, d, Bc, num_splits))
+
+
 def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                 Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None,
-                block_state=None, order: str = "ascending") -> Plan:
+                block_state=None, order: str = "ascending", max_scope: str = "sequence",
+                decisions: str = "group") -> Plan:
     """Marshal a decode (arguments as ``decode_fwd``) into a reusable Plan."""
     torch = _torch()
     B, Hq, d = q.shape
@@ -340,20 +352,25 @@ def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     a.counters, a.block_state = _ptr(counters), _ptr(block_state)
     a.block_order = _order_code(order)
+    a.max_scope = _choice_code("max_scope", max_scope, ("sequence", "split"))
+    a.decisions = _choice_code("decisions", decisions, ("group", "head"))
     keep = (q, k_cache, v_cache, workspace, counters, block_state)
     return Plan(library().bsattn_decode_fwd, a, out, keep)
 
 
 def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
-               order: str = "ascending", stream=None):
+               order: str = "ascending", max_scope: str = "sequence", decisions: str = "group", stream=None):
     """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
 
     ``workspace`` is a uint8 device tensor of at least
-    ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None)."""
+    ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None).
+    ``max_scope="split"`` restarts the running max at every split and
+    ``decisions="head"`` lets every query head decide for itself (variants;
+    ``block_state`` is then [B, Hq, Tc])."""
     return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
                        workspace=workspace, out=out, counters=counters, block_state=block_state,
-                       order=order)(stream)
+                       order=order, max_scope=max_scope, decisions=decisions)(stream)
 
 
 def calibrate_fit(target: float, lengths, lambdas, sparsity, delta: float):

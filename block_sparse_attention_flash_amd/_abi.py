@@ -22,7 +22,8 @@ EXPORTED = (
     "bsattn_status_string", "bsattn_last_error", "bsattn_version",
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
     "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
-    "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_fwd", "bsattn_decode_check",
+    "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
+    "bsattn_decode_fwd", "bsattn_decode_check",
     "bsattn_calibrate_threshold",
 )
 
@@ -63,7 +64,8 @@ class DecodeArgs(C.Structure):
                 ("q_stride", C.c_int64 * 2), ("kv_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 2),
                 ("scale", C.c_float), ("lam", C.c_float), ("Bc", C.c_int32), ("num_splits", C.c_int32),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("counters", C.c_void_p), ("block_state", C.c_void_p), ("block_order", C.c_int32)]
+                ("counters", C.c_void_p), ("block_state", C.c_void_p), ("block_order", C.c_int32),
+                ("max_scope", C.c_int32), ("decisions", C.c_int32)]
 
 
 def load(path: str = None) -> C.CDLL:
@@ -98,6 +100,8 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_decode_workspace_size.argtypes = [C.c_int32] * 7
     lib.bsattn_decode_num_splits.restype = C.c_int32
     lib.bsattn_decode_num_splits.argtypes = [C.c_int32] * 7
+    lib.bsattn_decode_split_blocks.restype = C.c_int32
+    lib.bsattn_decode_split_blocks.argtypes = [C.c_int32] * 7
     lib.bsattn_decode_fwd.restype = C.c_int
     lib.bsattn_decode_fwd.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
     lib.bsattn_decode_check.restype = C.c_int

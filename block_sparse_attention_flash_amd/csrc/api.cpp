@@ -227,6 +227,15 @@ int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, 
   return decode_choose_splits(B, Hkv, (L + Bc - 1) / Bc, Hq / Hkv, num_splits, &bps);
 }
 
+int32_t bsattn_decode_split_blocks(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d, int32_t Bc,
+                                   int32_t num_splits) {
+  (void)d;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || Bc < 1 || Hq % Hkv) return 0;
+  int32_t bps;
+  decode_choose_splits(B, Hkv, (L + Bc - 1) / Bc, Hq / Hkv, num_splits, &bps);
+  return bps;
+}
+
 bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   clear_error();
   if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
@@ -266,6 +275,10 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   if ((int64_t)a->B * a->Hkv * p.num_splits > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   p.workspace = a->workspace; p.counters = a->counters; p.block_state = a->block_state;
   p.block_order = a->block_order;
+  if (a->max_scope != 0 && a->max_scope != 1) return fail(BSATTN_ERR_INVALID_ARG, "max_scope must be 0 or 1");
+  if (a->decisions != 0 && a->decisions != 1) return fail(BSATTN_ERR_INVALID_ARG, "decisions must be 0 or 1");
+  p.split_reset = a->max_scope;
+  p.per_head = a->decisions;
   return hip_status(launch_decode(p, stream), "decode launch");
 }
 

@@ -76,6 +76,7 @@ struct DecSmem {
   float m_ref[G];
   float lsum[4][G];
   float pre[G];
+  uint64_t rskip[G];            // per-head variant: blocks each head skips (else 0)
   float pbuf[4][G][64];         // per-wave P of the kept block in flight
   int kept[64];
   int nkept;
@@ -187,7 +188,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   __syncthreads();
 
   // ---- publish aggregate, look back, publish inclusive prefix ----------------
-  if (tid == 0) {
+  // (per-split variant: no prefix, the running max starts afresh in the split)
+  if (tid == 0 && p.split_reset) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) sm.pre[r] = kNegInf;
+  } else if (tid == 0) {
     float agg[G];
 #pragma unroll
     for (int r = 0; r < G; ++r) {
@@ -233,20 +238,24 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
         if (x == kNegInf || x - cm < log2_lambda) agree |= (1ull << lb);
       }
     }
+    const uint64_t valid = nb == 64 ? ~0ull : ((1ull << nb) - 1ull);
+    const uint64_t own = dyn ? (agree & valid) : 0ull;  // this row's own test (lanes >= G: all)
     // all rows must agree
     for (int o = 1; o < 64; o <<= 1) {
       const uint64_t other = ((uint64_t)__shfl_xor((unsigned)(agree >> 32), o) << 32) |
                              (uint64_t)(unsigned)__shfl_xor((unsigned)agree, o);
       agree &= other;
     }
-    const uint64_t valid = nb == 64 ? ~0ull : ((1ull << nb) - 1ull);
-    const uint64_t skipm = dyn ? (agree & valid) : 0ull;
+    const uint64_t skipm = dyn ? (agree & valid) : 0ull;  // no head computes these
     const uint64_t keepm = valid & ~skipm;
     if (lane < G) {
+      // a row's reference max spans the blocks the row itself computes
+      const uint64_t rowkeep = valid & ~(p.per_head ? own : skipm);
       float mr = kNegInf;
       for (int lb = 0; lb < nb; ++lb)
-        if ((keepm >> lb) & 1ull) mr = fmaxf(mr, sm.bm[lb][lane]);
+        if ((rowkeep >> lb) & 1ull) mr = fmaxf(mr, sm.bm[lb][lane]);
       sm.m_ref[lane] = mr;
+      sm.rskip[lane] = p.per_head ? own : 0ull;
     }
     if (lane == 0) {
       int n = 0;
@@ -255,9 +264,16 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       sm.nkept = n;
       counts[unit] = __popcll(skipm);
     }
-    if (p.block_state)
+    if (p.block_state && p.per_head) {  // [B, Hq, Tc]: each head's own decisions
+      lds_fence();                       // sm.rskip written above by this wave
+      for (int x = lane; x < G * nb; x += 64) {
+        const int r = x / nb, lb = x % nb;
+        p.block_state[((int64_t)b * p.Hq + g * G + r) * p.Tc + blk0 + lb] = ((sm.rskip[r] >> lb) & 1ull) ? 2 : 1;
+      }
+    } else if (p.block_state) {
       for (int lb = lane; lb < nb; lb += 64)
         p.block_state[((int64_t)b * p.Hkv + g) * p.Tc + blk0 + lb] = ((skipm >> lb) & 1ull) ? 2 : 1;
+    }
   }
   __syncthreads();
   const int nkept = sm.nkept;
@@ -274,14 +290,19 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
   float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // rows 4*q16+i, keys of this lane
   float mref_l[4];
+  uint64_t rskip_l[4];  // per-head variant: a row's skipped blocks get P = 2^(s - inf) = 0
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * q16 + i;
     mref_l[i] = row < G ? sm.m_ref[row] : 0.0f;
+    rskip_l[i] = row < G ? sm.rskip[row] : 0ull;
   }
   for (int k = wave; k < nkept; k += 4) {
     const int lb = sm.kept[k];
     const int j = blk0 + lb;
+    float mb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mb[i] = ((rskip_l[i] >> lb) & 1ull) ? kPosInf : mref_l[i];
     bf16x8 kf[4][KS];
     load_k_block<D>(kf, kbase, p.ks_t, j, p.L, r16, q16);
     u32x4 vv[STEPS];
@@ -299,7 +320,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * q16 + i;
         if (row < G) {
-          const float e = fast_exp2(sc[kt][i] - mref_l[i]);  // 2^-inf = 0 for keys >= L
+          const float e = fast_exp2(sc[kt][i] - mb[i]);  // 2^-inf = 0 for keys >= L
           lpart[i] += e;
           sm.pbuf[wave][row][16 * kt + r16] = e;
         }

@@ -76,6 +76,8 @@ struct DecodeParams {
   int32_t* counters;
   uint8_t* block_state;
   int32_t block_order;
+  int32_t split_reset;     // running max restarts per split (variant)
+  int32_t per_head;        // skip decisions per query head (variant)
 };
 
 // Decode workspace layout (all offsets 256-byte aligned), see decode.hip.

@@ -233,16 +233,27 @@ typedef struct {
   float lambda;           /* [0, 1) */
   int32_t Bc;             /* 64 */
   int32_t num_splits;     /* splits per (sequence, K/V head); 0 = automatic.  Never changes results
-                             beyond float rounding order; never changes the skip set */
+                             beyond float rounding order; never changes the skip set (except under
+                             max_scope = 1, below) */
   void* workspace;        /* device, >= bsattn_decode_workspace_size(...) bytes, 256-byte aligned.
                              Tickets, flags and counters: zero-fill it once before its first use;
                              every call leaves them at zero again.  Calls that share a workspace
                              must not overlap (same stream, or ordered by events). */
   size_t workspace_bytes;
-  int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks */
-  uint8_t* block_state;   /* optional device [B, Hkv, Tc]: 1 computed, 2 skipped */
+  int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks, where a
+                             skipped block is one whose V block no head of the group loads */
+  uint8_t* block_state;   /* optional device [B, Hkv, Tc]: 1 computed, 2 skipped; with
+                             decisions = 1 it is [B, Hq, Tc], the decision of each query head */
   int32_t block_order;    /* 0: ascending key blocks (Algorithm 1); 1: descending, most recent
                              keys first (block-row reordering, BLASST notes) */
+  int32_t max_scope;      /* 0: the running max of the skip test spans the whole sequence in
+                             visiting order (Algorithm 1, exact whatever the split count);
+                             1: variant, the running max restarts at the first block of every
+                             split, so the skip set depends on num_splits */
+  int32_t decisions;      /* 0: one skip decision per group of G query heads sharing the K/V head
+                             (the tile of Algorithm 1), which lets a skipped V block go unloaded;
+                             1: variant, every query head decides for itself; a V block is then
+                             loaded when any head of the group keeps it */
 } bsattn_decode_args;
 
 /* Workspace bytes for a decode call with these sizes (num_splits as in the args). */
@@ -252,6 +263,12 @@ size_t bsattn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
 /* Splits per (sequence, K/V head) a call with these sizes would use. */
 int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
                                  int32_t Bc, int32_t num_splits);
+
+/* Key blocks per split of such a call: split s holds visiting positions
+ * [s * n, (s + 1) * n) of the block sequence (the last split may be shorter).
+ * Needed to state the skip set under max_scope = 1.  0 for invalid sizes. */
+int32_t bsattn_decode_split_blocks(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
+                                   int32_t Bc, int32_t num_splits);
 
 /* Enqueue the decode on `stream`: the split kernel, then the combine kernel
  * (merge of the splits, attention tutorial section 4.2). */

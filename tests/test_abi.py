@@ -117,6 +117,9 @@ BAD_DECODE = [
     ("Bc 128", lambda a: setattr(a, "Bc", 128), _abi.BSATTN_ERR_UNSUPPORTED),
     ("kv stride", lambda a: a.kv_stride.__setitem__(1, 2 * 128 + 1), _abi.BSATTN_ERR_UNSUPPORTED),
     ("negative splits", lambda a: setattr(a, "num_splits", -1), _abi.BSATTN_ERR_INVALID_ARG),
+    ("block order 2", lambda a: setattr(a, "block_order", 2), _abi.BSATTN_ERR_INVALID_ARG),
+    ("max scope 2", lambda a: setattr(a, "max_scope", 2), _abi.BSATTN_ERR_INVALID_ARG),
+    ("decisions -1", lambda a: setattr(a, "decisions", -1), _abi.BSATTN_ERR_INVALID_ARG),
 ]
 
 
@@ -138,5 +141,10 @@ def test_decode_split_policy():
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=4) == 4
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=1) == 1
     assert bsa.decode_num_splits(1, 4, 1, 128 * 64, 128, num_splits=1) == 2
+    # blocks per split: S = ceil(Tc / n)
+    assert bsa.decode_split_blocks(32, 32, 8, 131072, 128) == 64
+    assert bsa.decode_split_blocks(1, 4, 1, 64 * 10, 128, num_splits=3) == 4
+    assert bsa.decode_split_blocks(1, 4, 1, 128 * 64, 128, num_splits=1) == 64
+    assert bsa.decode_split_blocks(1, 4, 3, 64, 128) == 0                        # Hq % Hkv != 0
     assert bsa.decode_workspace_size(32, 32, 8, 131072, 128) > 32 * 8 * 32 * 4 * 128 * 4   # partial O of every split
     assert bsa.decode_workspace_size(0, 1, 1, 1, 64) == 0

@@ -33,16 +33,18 @@ def _shared_workspace(nbytes):
     return _WS[0]
 
 
-def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None, order="ascending"):
+def run_decode(cfg, q, kc, vc, *, L=None, num_splits=0, lam=None, order="ascending", max_scope="sequence",
+               decisions="group"):
     B, Hq, d = q.shape
     Hkv = kc.shape[2]
     L = kc.shape[1] if L is None else L
     Tc = -(-L // 64)
     ws = _shared_workspace(bsa.decode_workspace_size(B, Hq, Hkv, L, d, 64, num_splits))
-    state = torch.zeros((B, Hkv, Tc), dtype=torch.uint8, device=DEV)
+    state = torch.zeros((B, Hq if decisions == "head" else Hkv, Tc), dtype=torch.uint8, device=DEV)
     counters = torch.full((B, Hkv, 2), -1, dtype=torch.int32, device=DEV)
     out = bsa.decode_fwd(q, kc, vc, L=L, scale=cfg.scale, lam=cfg.lam if lam is None else lam,
-                         num_splits=num_splits, workspace=ws, counters=counters, block_state=state, order=order)
+                         num_splits=num_splits, workspace=ws, counters=counters, block_state=state, order=order,
+                         max_scope=max_scope, decisions=decisions)
     torch.cuda.synchronize()
     assert bsa.decode_check(ws) == 0, "decode look-back wait timed out"
     return out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
@@ -172,4 +174,77 @@ def test_decode_descending_order(num_splits):
             tot = [x + y for x, y in zip(tot, r)]
     asc = run_decode(cfg, qd, kd, vd, num_splits=num_splits, lam=0.3)
     _say(f"  skipped {tot[1]} of {tot[0]} (descending), {int(asc[2][..., 1].sum())} ascending at lambda 0.3")
+    assert tot[1] > 0
+
+
+def check_variant(q, k, v, out, st, cnt, b, L, scale, lam, order, split_blocks, decisions):
+    """check_sequence for the variants: per-split running max (split_blocks > 0)
+    and per-head decisions (block_state then holds one row per query head)."""
+    Hq = q.shape[0]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    Tc = -(-L // 64)
+    kw = dict(order=order, split_blocks=split_blocks, decisions=decisions)
+    ref, skip, margin = A.decode_sequence(q, k[:L], v[:L], 64, scale, lam, "closed_form", **kw)
+    per = G if decisions == "head" else 1
+    tot = [0, 0, 0]
+    for g in range(Hkv):
+        rows = slice(g * per, (g + 1) * per)
+        gs = st[b, rows] == 2
+        assert np.all(st[b, rows] != 0), "every block of the sequence is visited"
+        diff = gs != skip[rows]
+        excused = np.abs(margin[rows]) <= MARGIN
+        bad = diff & ~excused
+        assert not bad.any(), f"skip set differs b{b} g{g}: {np.argwhere(bad)} margins {margin[rows][bad]}"
+        r = ref[g * G:(g + 1) * G]
+        if diff.any():
+            if decisions == "head":
+                force = {(int(h), int(j)): bool(gs[h, j]) for h, j in np.argwhere(diff)}
+            else:
+                force = {int(j): bool(gs[0, j]) for j in np.nonzero(diff[0])[0]}
+            r, _, _ = A.decode_group(q[g * G:(g + 1) * G], k[:L, g], v[:L, g], 64, scale, lam, "closed_form", force,
+                                     **kw)
+        v_skipped = int(gs.all(axis=0).sum())         # blocks no head of the group computes
+        assert cnt[b, g, 0] == Tc and cnt[b, g, 1] == v_skipped
+        compare_out(A.as_f64(out[b, g * G:(g + 1) * G]), r, False, f"decode variant b{b} g{g}")
+        tot[0] += gs.size
+        tot[1] += int(gs.sum())
+        tot[2] += v_skipped
+    return tot
+
+
+VARIANTS = [
+    # (max_scope, decisions, order, num_splits, G, d)
+    ("split", "group", "ascending", 7, 4, 128),
+    ("split", "group", "ascending", 0, 8, 64),
+    ("split", "group", "descending", 3, 4, 128),
+    ("split", "group", "ascending", 1, 2, 128),
+    ("sequence", "head", "ascending", 0, 4, 128),
+    ("sequence", "head", "ascending", 7, 8, 64),
+    ("sequence", "head", "descending", 5, 4, 128),
+    ("split", "head", "ascending", 4, 4, 64),
+]
+
+
+@pytest.mark.parametrize("max_scope,decisions,order,num_splits,G,d", VARIANTS,
+                         ids=["-".join(str(x) for x in v) for v in VARIANTS])
+def test_decode_variants(max_scope, decisions, order, num_splits, G, d):
+    """Per-split running max and per-head decisions against the oracle's
+    variants: skip sets (per head where heads decide), the counters (blocks
+    whose V load no head needs) and outputs."""
+    L = 4100
+    Hkv = 2
+    cfg = DecodeWorkload(name="s", description="", B=2, Hq=G * Hkv, Hkv=Hkv, L=L, d=d, Bc=64, lam=40.0 / L, seed=31)
+    _say(f"decode variant {max_scope}/{decisions}/{order}, splits {num_splits}, G{G} d{d}")
+    q, kc, vc = gen_decode_inputs(cfg)
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    bps = bsa.decode_split_blocks(cfg.B, cfg.Hq, Hkv, L, d, 64, num_splits) if max_scope == "split" else 0
+    tot = [0, 0, 0]
+    for lam in (cfg.lam, 0.05, 0.4):
+        out, st, cnt = run_decode(cfg, qd, kd, vd, num_splits=num_splits, lam=lam, order=order,
+                                  max_scope=max_scope, decisions=decisions)
+        for b in range(cfg.B):
+            r = check_variant(q[b], kc[b], vc[b], out, st, cnt, b, L, cfg.scale, lam, order, bps, decisions)
+            tot = [x + y for x, y in zip(tot, r)]
+    _say(f"  decisions {tot[0]}, skipped {tot[1]}, V blocks not loaded {tot[2]}")
     assert tot[1] > 0
