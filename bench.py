@@ -352,6 +352,57 @@ def sweep_decode(name: str, lams, steps: int, warmup: int):
     return {"workload": name, "description": cfg.description, "points": res}
 
 
+DECODE_VARIANTS = [
+    # (order, max_scope, decisions, num_splits): the first is Algorithm 1 as the pages give it
+    ("ascending", "sequence", "group", 0),
+    ("ascending", "split", "group", 0),
+    ("ascending", "split", "group", 256),
+    ("ascending", "sequence", "head", 0),
+    ("descending", "sequence", "group", 0),
+]
+
+
+def decode_variants(name: str, lams, steps: int, warmup: int):
+    """Order and decision variants of the decode on one workload: time, the
+    share of V blocks no head loads, and the share of per-head (or per-group)
+    decisions that skip."""
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_decode_inputs
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"variants {name}: generating inputs ({cfg.description})")
+    q, kc, vc = gen_decode_inputs(cfg, device=dev)
+    Tc = -(-cfg.L // cfg.Bc)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.bfloat16, device=dev)
+    res = []
+    for lam in lams:
+        for order, scope, dec, ns in DECODE_VARIANTS:
+            ws = bsa.decode_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, dev, cfg.Bc, ns)
+            cnt = torch.zeros((cfg.B, cfg.Hkv, 2), dtype=torch.int32, device=dev)
+            st = torch.zeros((cfg.B, cfg.Hq if dec == "head" else cfg.Hkv, Tc), dtype=torch.uint8, device=dev)
+            mk = lambda c=None, b=None: bsa.decode_plan(q, kc, vc, L=cfg.L, scale=cfg.scale, lam=lam, Bc=cfg.Bc,
+                                                        num_splits=ns, workspace=ws, out=out, counters=c,
+                                                        block_state=b, order=order, max_scope=scope, decisions=dec)
+            mk(cnt, st)()
+            torch.cuda.synchronize()
+            c = cnt.view(-1, 2).sum(0).tolist()
+            dec_skip = float((st == 2).float().mean().item())
+            t = time_launches(mk(), steps, warmup)
+            bps = bsa.decode_split_blocks(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.Bc, ns)
+            res.append({"lambda": lam, "order": order, "max_scope": scope, "decisions": dec,
+                        "blocks_per_split": bps, "ms": t["ms_per_step"],
+                        "pct_V_blocks_skipped": 100.0 * c[1] / max(1, c[0]),
+                        "pct_decisions_skip": 100.0 * dec_skip, "health": bsa.decode_check(ws)})
+            log(f"variants {name} lambda {lam:.3g} {order}/{scope}/{dec} bps {bps}: {t['ms_per_step']:.4f} ms, "
+                f"V skipped {res[-1]['pct_V_blocks_skipped']:.2f}%, decisions skip {100 * dec_skip:.2f}%")
+            del ws, st
+    del q, kc, vc, out
+    torch.cuda.empty_cache()
+    return {"workload": name, "description": cfg.description, "points": res}
+
+
 def calibration_demo(target: float = 0.5, delta: float = 0.05):
     """BLASST threshold calibration (notes section 3.2, Algorithm 2) on the
     synthetic decode recipe at several context lengths, and the comparison
@@ -457,6 +508,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the metric line: a lambda sweep (static + dynamic skipping together) per "
                          "workload, as one JSON line")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the metric line: the decode order and decision variants on the decode workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
@@ -483,9 +536,14 @@ def main(argv=None) -> int:
             fn = sweep_decode if name == "cfg5" else sweep_prefill
             rep.append(fn(name, lams, min(a.steps, 50) if name != "cfg2" else a.steps, min(a.warmup, 20)
                           if name != "cfg2" else a.warmup))
+        var = decode_variants("cfg5", [40.0 / 131072, 1e-2, 0.1], min(a.steps, 50), min(a.warmup, 20))
         cal = calibration_demo()
-        print(json.dumps({"sweep": rep, "calibration": cal, "steps": a.steps,
+        print(json.dumps({"sweep": rep, "decode_variants": var, "calibration": cal, "steps": a.steps,
                           "device": torch.cuda.get_device_name(0)}))
+        return 0
+    if a.variants:
+        var = decode_variants("cfg5", [40.0 / 131072, 1e-2, 0.1], min(a.steps, 50), min(a.warmup, 20))
+        print(json.dumps({"decode_variants": var, "device": torch.cuda.get_device_name(0)}))
         return 0
     if a.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
