@@ -14,6 +14,9 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``build_schedule(row_ptr, max_blocks_per_item)`` -> Schedule (host arrays, counts)
 * ``prefill_workspace_size(B, Hq, d, n_slots)``, ``prefill_workspace(...)`` (zero-filled)
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
+* ``prefill_bwd(q, k, v, out, dout, lse, ...)`` -> (dq, dk, dv) for a static mask;
+  ``transpose_block_index(row_ptr, col_idx, Tc)`` -> (col_ptr, row_idx),
+  ``prefill_bwd_workspace_size(B, Hq, Nq)``
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
 * ``calibrate_fit(...)``, ``calibrate(target, lengths, lambdas, delta, measure)``,
   ``decode_sparsity(...)``: threshold calibration lambda = a / L
@@ -35,7 +38,10 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
-    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace", "prefill_fwd", "prefill_plan", "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits", "decode_split_blocks", "decode_check",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace",
+    "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_workspace_size", "transpose_block_index",
+    "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits",
+    "decode_split_blocks", "decode_check",
     "calibrate_fit", "calibrate", "decode_sparsity",
 ]
 
@@ -120,6 +126,18 @@ def validate_block_index(row_ptr, col_idx, Tc: int):
     col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
     _check(library().bsattn_validate_block_index(row_ptr.ctypes.data, col_idx.ctypes.data if col_idx.size else None,
                                                  row_ptr.size - 1, Tc))
+
+
+def transpose_block_index(row_ptr, col_idx, Tc: int):
+    """CSR (tiles -> key blocks) to CSC (key blocks -> tiles), host int32 arrays."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    Tr = row_ptr.size - 1
+    col_ptr = np.zeros(Tc + 1, np.int32)
+    row_idx = np.zeros(max(1, int(row_ptr[-1])), np.int32)
+    _check(library().bsattn_transpose_block_index(row_ptr.ctypes.data, col_idx.ctypes.data, Tr, int(Tc),
+                                                  col_ptr.ctypes.data, row_idx.ctypes.data))
+    return col_ptr, row_idx[:int(row_ptr[-1])].copy()
 
 
 def tile_order_lpt(row_ptr):
@@ -232,7 +250,8 @@ class Plan:
 def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                  Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
                  out=None, tile_counters=None, block_state=None, row_counters=None,
-                 schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending") -> Plan:
+                 schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending",
+                 lse=None) -> Plan:
     """Marshal a prefill (arguments as ``prefill_fwd``) into a reusable Plan."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
@@ -265,6 +284,7 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
     a.tile_counters, a.block_state = _ptr(tile_counters), _ptr(block_state)
     a.row_counters = _ptr(row_counters)
     a.block_order = _order_code(order)
+    a.lse = _ptr(lse)
     if schedule is not None:
         if schedule.d_items is None:
             schedule.to(q.device)
@@ -275,14 +295,16 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
                 workspace = prefill_workspace(B, Hq, d, schedule.n_slots, q.device)
             a.workspace = _ptr(workspace)
             a.workspace_bytes = int(workspace.numel() * workspace.element_size())
-    keep = (q, k, v, row_ptr, col_idx, tile_order, tile_counters, block_state, row_counters, schedule, workspace)
+    keep = (q, k, v, row_ptr, col_idx, tile_order, tile_counters, block_state, row_counters, schedule, workspace,
+            lse)
     return Plan(library().bsattn_prefill_fwd, a, out, keep)
 
 
 def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, causal: bool = False,
                 Br: int = 128, Bc: int = 64, row_ptr=None, col_idx=None, tile_order=None, n_valid: int = 0,
                 out=None, tile_counters=None, block_state=None, row_counters=None,
-                schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending", stream=None):
+                schedule: Optional[Schedule] = None, workspace=None, order: str = "ascending", lse=None,
+                stream=None):
     """Block-sparse / BLASST attention forward, q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (last dim contiguous).
 
     ``row_ptr``/``col_idx``/``tile_order`` are int32 device tensors (or None);
@@ -293,12 +315,57 @@ def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, cau
     BLASST notes' block-row reordering).  ``schedule`` (from
     ``build_schedule``, device copies made with ``.to``) cuts long tiles;
     its partials go to ``workspace`` (a uint8 device tensor from
-    ``prefill_workspace``, allocated here if None).  Returns ``out``."""
+    ``prefill_workspace``, allocated here if None).  ``lse`` float32
+    [B, Hq, Nq] optionally receives each row's natural-log sum of exp of
+    its attended scores (input of ``prefill_bwd``).  Returns ``out``."""
     return prefill_plan(q, k, v, scale=scale, lam=lam, causal=causal, Br=Br, Bc=Bc, row_ptr=row_ptr,
                         col_idx=col_idx, tile_order=tile_order, n_valid=n_valid, out=out,
                         tile_counters=tile_counters, block_state=block_state, row_counters=row_counters,
                         schedule=schedule, order=order,
-                        workspace=workspace)(stream)
+                        workspace=workspace, lse=lse)(stream)
+
+
+def prefill_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
+    return int(library().bsattn_prefill_bwd_workspace_size(B, Hq, Nq))
+
+
+def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
+                row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the static block-sparse forward (lambda = 0) for the loss
+    sum(out * dout): q, out, dout [B, Nq, Hq, d], k, v [B, Nk, Hkv, d] bf16,
+    ``lse`` float32 [B, Hq, Nq] from ``prefill_fwd(..., lse=)``.  The mask
+    arguments are the forward's; with a CSR, ``col_ptr``/``row_idx`` are the
+    device copies of ``transpose_block_index``.  Returns (dq, dk, dv)."""
+    torch = _torch()
+    if q.dtype != torch.bfloat16:
+        raise BsattnError(_abi.BSATTN_ERR_UNSUPPORTED, "the backward is implemented for bf16")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(prefill_bwd_workspace_size(B, Hq, Nq), dtype=torch.uint8, device=q.device)
+    a = _abi.BwdArgs()
+    a.dtype = _abi.BSATTN_BF16
+    a.q, a.k, a.v, a.out, a.dout = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout)
+    a.lse, a.dq, a.dk, a.dv = _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv)
+    a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d = B, Hq, Hkv, Nq, Nk, d
+    for fld, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out), ("do_stride", dout),
+                   ("dq_stride", dq), ("dk_stride", dk), ("dv_stride", dv)):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, f"{fld[:-7]} must be [B, N, H, d] with d contiguous")
+        getattr(a, fld)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    a.row_ptr, a.col_idx, a.col_ptr, a.row_idx = _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx)
+    a.n_valid = int(n_valid)
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.causal = 1 if causal else 0
+    a.Br, a.Bc = 128, 64
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    _check(library().bsattn_prefill_bwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
+    return dq, dk, dv
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:

@@ -22,6 +22,7 @@ EXPORTED = (
     "bsattn_status_string", "bsattn_last_error", "bsattn_version",
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
     "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
+    "bsattn_transpose_block_index", "bsattn_prefill_bwd_workspace_size", "bsattn_prefill_bwd",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
     "bsattn_decode_fwd", "bsattn_decode_check",
     "bsattn_calibrate_threshold",
@@ -54,7 +55,21 @@ class PrefillArgs(C.Structure):
                 ("block_order", C.c_int32),
                 ("sched_items", C.c_void_p), ("n_items", C.c_int32), ("sched_merges", C.c_void_p),
                 ("n_merges", C.c_int32), ("n_slots", C.c_int32), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t)]
+                ("workspace_bytes", C.c_size_t), ("lse", C.c_void_p)]
+
+
+class BwdArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32),
+                ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p), ("out", C.c_void_p), ("dout", C.c_void_p),
+                ("lse", C.c_void_p), ("dq", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p),
+                ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("Nq", C.c_int32), ("Nk", C.c_int32),
+                ("d", C.c_int32),
+                ("q_stride", C.c_int64 * 3), ("k_stride", C.c_int64 * 3), ("v_stride", C.c_int64 * 3),
+                ("o_stride", C.c_int64 * 3), ("do_stride", C.c_int64 * 3), ("dq_stride", C.c_int64 * 3),
+                ("dk_stride", C.c_int64 * 3), ("dv_stride", C.c_int64 * 3),
+                ("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("col_ptr", C.c_void_p), ("row_idx", C.c_void_p),
+                ("n_valid", C.c_int32), ("scale", C.c_float), ("causal", C.c_int32), ("Br", C.c_int32),
+                ("Bc", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
 class DecodeArgs(C.Structure):
@@ -96,6 +111,13 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_prefill_workspace_size.argtypes = [C.c_int32] * 4
     lib.bsattn_prefill_fwd.restype = C.c_int
     lib.bsattn_prefill_fwd.argtypes = [C.POINTER(PrefillArgs), C.c_void_p]
+    lib.bsattn_transpose_block_index.restype = C.c_int
+    lib.bsattn_transpose_block_index.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
+                                                 C.c_void_p]
+    lib.bsattn_prefill_bwd_workspace_size.restype = C.c_size_t
+    lib.bsattn_prefill_bwd_workspace_size.argtypes = [C.c_int32] * 3
+    lib.bsattn_prefill_bwd.restype = C.c_int
+    lib.bsattn_prefill_bwd.argtypes = [C.POINTER(BwdArgs), C.c_void_p]
     lib.bsattn_decode_workspace_size.restype = C.c_size_t
     lib.bsattn_decode_workspace_size.argtypes = [C.c_int32] * 7
     lib.bsattn_decode_num_splits.restype = C.c_int32

@@ -24,7 +24,7 @@ LIB = os.path.join(LIBDIR, "libbsattn.so")
 ARCH = os.environ.get("BSATTN_ARCH", "gfx950")
 
 HOST_SOURCES = ["api.cpp", "block_index.cpp", "calibrate.cpp"]
-DEVICE_SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+DEVICE_SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "prefill_bwd.hip", "decode.hip"]
 
 
 def hipcc() -> str:

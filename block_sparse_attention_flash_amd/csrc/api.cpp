@@ -173,6 +173,7 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   p.Tc = (a->Nk + a->Bc - 1) / a->Bc;
   p.tile_counters = a->tile_counters; p.block_state = a->block_state;
   p.row_counters = a->row_counters;
+  p.lse = a->lse;
   if (a->block_order != 0 && a->block_order != 1) return fail(BSATTN_ERR_INVALID_ARG, "block_order must be 0 or 1");
   p.block_order = a->block_order;
   if (a->sched_items) {
@@ -203,6 +204,67 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   if ((int64_t)p.B * p.Hq * units > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   int e = a->dtype == BSATTN_BF16 ? launch_prefill_bf16(p, stream) : launch_prefill_f32(p, stream);
   return hip_status(e, "prefill launch");
+}
+
+size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Nq) {
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  return align256((size_t)B * Hq * Nq * sizeof(float));
+}
+
+bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the backward is implemented for bf16");
+  const void* ptrs[] = {a->q, a->k, a->v, a->out, a->dout, a->dq, a->dk, a->dv};
+  for (const void* x : ptrs) {
+    if (!x) return fail(BSATTN_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be non-NULL");
+    if (!aligned16(x)) return fail(BSATTN_ERR_UNSUPPORTED, "q, k, v, out, dout, dq, dk, dv must be 16-byte aligned");
+  }
+  if (!a->lse || (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return fail(BSATTN_ERR_INVALID_ARG, "lse must be a non-NULL float array");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Nq < 1 || a->Nk < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "B, Hq, Hkv, Nq, Nk must be >= 1");
+  if (a->Hq % a->Hkv != 0) return fail(BSATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", a->d);
+  bsattn_status st;
+  const struct { const char* n; const int64_t* s; } strides[] = {
+      {"q", a->q_stride},   {"k", a->k_stride},   {"v", a->v_stride},   {"out", a->o_stride},
+      {"dout", a->do_stride}, {"dq", a->dq_stride}, {"dk", a->dk_stride}, {"dv", a->dv_stride}};
+  for (const auto& x : strides)
+    if ((st = check_strides(x.n, x.s, 3, 8)) != BSATTN_OK) return st;
+  if ((a->row_ptr == nullptr) != (a->col_idx == nullptr) || (a->row_ptr == nullptr) != (a->col_ptr == nullptr) ||
+      (a->row_ptr == nullptr) != (a->row_idx == nullptr))
+    return fail(BSATTN_ERR_INVALID_ARG, "row_ptr, col_idx, col_ptr, row_idx must all be set or all be NULL");
+  if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return fail(BSATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (a->causal && a->Nq != a->Nk) return fail(BSATTN_ERR_INVALID_ARG, "causal attention requires Nq == Nk");
+  if (a->n_valid < 0 || a->n_valid > a->Nk) return fail(BSATTN_ERR_INVALID_ARG, "n_valid must lie in [0, Nk]");
+  if (a->Br != 128 || a->Bc != 64) return fail(BSATTN_ERR_UNSUPPORTED, "the backward needs Br = 128, Bc = 64");
+  if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
+    return fail(BSATTN_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  const size_t need = bsattn_prefill_bwd_workspace_size(a->B, a->Hq, a->Nq);
+  if (a->workspace_bytes < need) return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, need);
+  BwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.dout = a->dout; p.lse = a->lse;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.dvec = static_cast<float*>(a->workspace);
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Nk = a->Nk; p.d = a->d;
+  p.qs_b = a->q_stride[0]; p.qs_t = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.ks_b = a->k_stride[0]; p.ks_t = a->k_stride[1]; p.ks_h = a->k_stride[2];
+  p.vs_b = a->v_stride[0]; p.vs_t = a->v_stride[1]; p.vs_h = a->v_stride[2];
+  p.os_b = a->o_stride[0]; p.os_t = a->o_stride[1]; p.os_h = a->o_stride[2];
+  p.dos_b = a->do_stride[0]; p.dos_t = a->do_stride[1]; p.dos_h = a->do_stride[2];
+  p.dqs_b = a->dq_stride[0]; p.dqs_t = a->dq_stride[1]; p.dqs_h = a->dq_stride[2];
+  p.dks_b = a->dk_stride[0]; p.dks_t = a->dk_stride[1]; p.dks_h = a->dk_stride[2];
+  p.dvs_b = a->dv_stride[0]; p.dvs_t = a->dv_stride[1]; p.dvs_h = a->dv_stride[2];
+  p.row_ptr = a->row_ptr; p.col_idx = a->col_idx; p.col_ptr = a->col_ptr; p.row_idx = a->row_idx;
+  p.n_valid = a->n_valid == 0 ? a->Nk : a->n_valid;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.Tr = (a->Nq + 127) / 128;
+  p.Tc = (a->Nk + 63) / 64;
+  if ((int64_t)p.B * p.Hq * p.Tr > 0x7fffffffLL || (int64_t)p.B * p.Hkv * p.Tc > 0x7fffffffLL ||
+      (int64_t)p.B * p.Hq * p.Nq > 0x7fffffffLL)
+    return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  return hip_status(launch_prefill_bwd(p, stream), "prefill backward launch");
 }
 
 size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n_slots) {

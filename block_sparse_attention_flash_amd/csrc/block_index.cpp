@@ -246,6 +246,25 @@ bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t*
   return BSATTN_OK;
 }
 
+bsattn_status bsattn_transpose_block_index(const int32_t* row_ptr, const int32_t* col_idx, int32_t Tr, int32_t Tc,
+                                           int32_t* col_ptr, int32_t* row_idx) {
+  using namespace bsattn;
+  clear_error();
+  if (!col_ptr || (!row_idx && row_ptr && row_ptr[Tr] > 0))
+    return fail(BSATTN_ERR_INVALID_ARG, "col_ptr / row_idx NULL");
+  const bsattn_status st = bsattn_validate_block_index(row_ptr, col_idx, Tr, Tc);
+  if (st != BSATTN_OK) return st;
+  // counting sort by key block; walking the tiles in ascending order keeps
+  // every key block's tile list ascending
+  for (int32_t c = 0; c <= Tc; ++c) col_ptr[c] = 0;
+  for (int32_t e = 0; e < row_ptr[Tr]; ++e) ++col_ptr[col_idx[e] + 1];
+  for (int32_t c = 0; c < Tc; ++c) col_ptr[c + 1] += col_ptr[c];
+  std::vector<int32_t> fill(col_ptr, col_ptr + Tc);
+  for (int32_t t = 0; t < Tr; ++t)
+    for (int32_t e = row_ptr[t]; e < row_ptr[t + 1]; ++e) row_idx[fill[col_idx[e]]++] = t;
+  return BSATTN_OK;
+}
+
 bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t max_blocks, int32_t* items,
                                     int32_t items_capacity, int32_t* merges, int32_t merges_capacity, int32_t* n_items,
                                     int32_t* n_merges, int32_t* n_slots) {

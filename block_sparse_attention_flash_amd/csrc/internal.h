@@ -50,7 +50,40 @@ struct PrefillParams {
   int32_t* part_cnt;            // [n_slots][B][Hq][2]
   int32_t* arrive;              // [n_merges][B][Hq] chunk arrival counters (zero between calls)
   int32_t rank_major;           // bf16 kernel: XCD work order (set by its launcher)
+  float* lse;                   // optional [B][Hq][Nq] natural-log row sums of exp
 };
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;                  // [B][Hq][Nq] rowsum(dout * out)
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int64_t dos_b, dos_t, dos_h;
+  int64_t dqs_b, dqs_t, dqs_h;
+  int64_t dks_b, dks_t, dks_h;
+  int64_t dvs_b, dvs_t, dvs_h;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* col_ptr;
+  const int32_t* row_idx;
+  int32_t n_valid;
+  float scale;
+  int32_t causal;
+  int32_t Tr, Tc;
+};
+
+int launch_prefill_bwd(const BwdParams& p, void* stream);
 
 struct PrefillWorkspace {
   size_t o, ml, cnt, arrive, total;

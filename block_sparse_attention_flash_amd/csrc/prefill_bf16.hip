@@ -562,6 +562,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       }
     }
     l_tot = l;
+    m_ref = M;
     if (p.tile_counters && tid == 0) {
       vis_tot = skip_tot = 0;
       for (int sl = s0; sl < s0 + ns; ++sl) {
@@ -587,6 +588,8 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       }
     }
   }
+  if (p.lse && row_ok && hi == 0)  // ln(sum exp(scale s)) = m scale + ln(l), l relative to m_ref
+    p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] = l_tot > 0.0f ? fmaf(m_ref, p.scale, logf(l_tot)) : kNegInf;
   if (p.tile_counters && tid == 0) {
     int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);
     tc[0] = vis_tot;

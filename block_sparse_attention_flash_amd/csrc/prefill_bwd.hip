@@ -1,0 +1,402 @@
+// bf16 backward of static block-sparse attention on CDNA4 matrix cores.
+//
+// For the loss sum(out * dout) of the forward out = softmax(scale Q K^T) V
+// over the block mask (tiles of 128 query rows x blocks of 64 keys, plus the
+// token-level valid-length and causal limits), with P rebuilt from the
+// forward's per-row log-sum-exp:
+//
+//   dot   Dv[i] = sum_c dout[i][c] out[i][c]            (one float per row)
+//   dkdv  per (batch, K/V head, key block j): walk the query tiles whose CSR
+//         list holds j (the transposed index), for every query head of the
+//         group, and accumulate in registers
+//            S  = Q K_j^T,  P = 2^(S c2 - lse log2e)    (masked entries 0)
+//            dP = dO V_j^T, dS = P (dP - Dv)
+//            dV_j^T += dO^T P,   dK_j^T += Q^T dS
+//   dq    per (batch, head, query tile): walk the tile's CSR list
+//            S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - Dv)
+//            dQ^T += K^T dS^T
+//
+// Every product is a v_mfma_f32_32x32x16_bf16.  An accumulator in layout
+// D[m][n] (lane n % 32, rows 8(a/4) + 4(l/32) + a%4 in element a) is the B
+// operand of a product that contracts over m, after a bf16 pack: the
+// contraction index runs through the same permutation in both operands, and
+// the other operand is read with ds_read_b64_tr_b16 in that order.  So P and
+// dS never leave registers.  Each kernel owns its outputs: no atomics, and
+// the results do not depend on scheduling.
+//
+// The pages print no backward pass; the gradients are the chain rule on the
+// forward's definition (the DiT article trains with the block-sparse
+// forward, section 4; its section 3.3 check of the block list before any
+// load applies to both walks here).
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int BR = 128;
+constexpr int BC = 64;
+constexpr int NT = 256;
+
+// R x D bf16 tile in LDS read both row-wise (16-byte chunks: MFMA operand
+// rows) and transposed (ds_read_b64_tr_b16 over 8 rows x 4 chunks).  Chunk c
+// of row r sits at r * CH + (c ^ swz(r)).  swz depends on r % 8 only, so a
+// transposed read 8 or 16 rows further down keeps its pattern; the 4 rows
+// of a transposed read fall into 4 different 64-byte bank groups, and 16
+// consecutive rows of a row read use 8 different chunks (a 2-way conflict).
+template <int D>
+struct BTile {
+  static constexpr int CH = D / 8;
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 1) : 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1);
+  }
+  __device__ static __forceinline__ int pos(int r, int c) { return (r * CH + (c ^ swz(r))) * 8; }
+};
+
+// Copy rows [0, nrows) of a R x D global tile (row stride in elements) into
+// LDS; rows >= nrows are zero-filled.
+template <int D, int R>
+__device__ __forceinline__ void stage_tile(__bf16* tile, const __bf16* src, int64_t stride, int nrows, int tid) {
+  constexpr int CH = D / 8;
+  constexpr int PER = R * CH / NT;
+  bf16x8 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int x = i * NT + tid;
+    const int r = x / CH, c = x % CH;
+    v[i] = r < nrows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * stride + 8 * c) : bf16x8{};
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int x = i * NT + tid;
+    const int r = x / CH, c = x % CH;
+    *reinterpret_cast<bf16x8*>(tile + BTile<D>::pos(r, c)) = v[i];
+  }
+}
+
+// Row fragment: X[r][16 ks + 8 hi + 0..7] (A operand rows, or B operand columns).
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const __bf16* tile, int r, int ks, int hi) {
+  return *reinterpret_cast<const bf16x8*>(tile + BTile<D>::pos(r, 2 * ks + hi));
+}
+
+// Transposed fragment (A operand X^T[m = d][k]): lane l gets, in slot i,
+// X[r0 + 8 (i/4) + 4 (l/32) + i%4][32 n + l%32], the row order of the
+// accumulator layout above.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const __bf16* tile, int r0, int n, int lane) {
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int r = r0 + 4 * (g16 >> 1) + (j16 >> 2);
+  const int c = 4 * n + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int half = 4 * (j16 & 1);
+  return join_bf16x4(lds_read_tr16(tile + BTile<D>::pos(r, c) + half),
+                     lds_read_tr16(tile + BTile<D>::pos(r + 8, c) + half));
+}
+
+// Dv = rowsum(dout * out), fp32, one row per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_dot_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
+  const int64_t rid = gid / LPR;  // (b, h, i) with i fastest
+  const int c = (int)(gid % LPR);
+  const int64_t total = (int64_t)p.B * p.Hq * p.Nq;
+  float acc = 0.0f;
+  if (rid < total) {
+    const int i = (int)(rid % p.Nq);
+    const int bh = (int)(rid / p.Nq);
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.out) + (int64_t)b * p.os_b +
+                                                     (int64_t)i * p.os_t + (int64_t)h * p.os_h + 8 * c);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b +
+                                                     (int64_t)i * p.dos_t + (int64_t)h * p.dos_h + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o);
+  if (rid < total && c == 0) p.dvec[rid] = acc;
+}
+
+// Store 4 consecutive d values (accumulator elements 4q..4q+3 of tile n) as bf16.
+__device__ __forceinline__ void store4(__bf16* dst, const f32x16& acc, int q4, float s) {
+  f32x4 v4 = {acc[4 * q4 + 0] * s, acc[4 * q4 + 1] * s, acc[4 * q4 + 2] * s, acc[4 * q4 + 3] * s};
+  *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v4, bf16x4);
+}
+
+template <int D>
+struct DkdvSmem {
+  __bf16 q[BR * D];
+  __bf16 g[BR * D];   // dout
+  float lse2[BR];     // lse in log2 units
+  float dv[BR];
+};
+
+// Work-groups per CU the dK/dV kernel's registers are cut for: at d = 128 the
+// K and V fragments (64 registers) and the dK and dV accumulators (128) leave
+// no room for a second group without spilling.
+template <int D>
+constexpr int kDkdvBlocksPerCu = D == 64 ? 2 : 1;
+
+// One work-group per (batch, K/V head, key block).  Wave w: keys 32 (w & 1)
+// .. +31 of the block (kh), query rows 64 (w >> 1) .. +63 of each tile (qh).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KS = D / 16;
+  constexpr int NTD = D / 32;
+  __shared__ DkdvSmem<D> sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int j = blockIdx.x % p.Tc;
+  const int bg = blockIdx.x / p.Tc;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const float c2 = p.scale * kLog2e;
+
+  // K and V rows of this lane's key as B operands: X[key][16 ks + 8 hi + 0..7]
+  const int key = j * BC + 32 * kh + l32;
+  const bool key_in = key < p.Nk;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = key_in ? *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * p.ks_t + 16 * ks + 8 * hi) : bf16x8{};
+    vf[ks] = key_in ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * p.vs_t + 16 * ks + 8 * hi) : bf16x8{};
+  }
+  const bool key_ok = key < p.n_valid;
+
+  f32x16 dk[NTD], dv[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
+
+  // query tiles that attend block j: the transposed CSR, or every tile (from
+  // the diagonal on when causal)
+  int e0, e1;
+  if (p.col_ptr) {
+    e0 = p.col_ptr[j];
+    e1 = p.col_ptr[j + 1];
+  } else {
+    e0 = CAUSAL ? (j * BC) / BR : 0;
+    e1 = p.Tr;
+  }
+  e0 = __builtin_amdgcn_readfirstlane(e0);
+  e1 = __builtin_amdgcn_readfirstlane(e1);
+  const int ntile = e1 - e0;
+
+  for (int it = 0; it < G * ntile; ++it) {
+    const int hh = it / ntile;
+    const int e = e0 + it % ntile;
+    const int t = __builtin_amdgcn_readfirstlane(p.row_idx ? p.row_idx[e] : e);
+    if (CAUSAL && t * BR + BR - 1 < j * BC) continue;  // wholly above the diagonal: not visited
+    const int h = g * G + hh;
+    const int nrows = min(BR, p.Nq - t * BR);
+    __syncthreads();  // the previous tile's LDS reads are done
+    stage_tile<D, BR>(sm.q, static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)(t * BR) * p.qs_t +
+                                (int64_t)h * p.qs_h, p.qs_t, nrows, tid);
+    stage_tile<D, BR>(sm.g, static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b +
+                                (int64_t)(t * BR) * p.dos_t + (int64_t)h * p.dos_h, p.dos_t, nrows, tid);
+    if (tid < BR) {
+      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + t * BR + tid;
+      sm.lse2[tid] = tid < nrows ? p.lse[ri] * kLog2e : 0.0f;
+      sm.dv[tid] = tid < nrows ? p.dvec[ri] : 0.0f;
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = qh * 64 + 32 * c;  // first tile row of this chunk
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(read_row<D>(sm.q, r0 + l32, ks, hi), kf[ks], s);   // S[q][key]
+        dp = mfma32(read_row<D>(sm.g, r0 + l32, ks, hi), vf[ks], dp);  // dP[q][key]
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int rl = r0 + 8 * (a >> 2) + 4 * hi + (a & 3);
+        const int row = t * BR + rl;
+        const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row);
+        pv[a] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse2[rl])) : 0.0f;
+        dsv[a] = pv[a] * (dp[a] - sm.dv[rl]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 pb = to_bf16x8(pv + 8 * kk);
+        const bf16x8 db = to_bf16x8(dsv + 8 * kk);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) {
+          dv[n] = mfma32(read_tr<D>(sm.g, r0 + 16 * kk, n, lane), pb, dv[n]);  // dV^T += dO^T P
+          dk[n] = mfma32(read_tr<D>(sm.q, r0 + 16 * kk, n, lane), db, dk[n]);  // dK^T += Q^T dS
+        }
+      }
+    }
+  }
+
+  // the two query halves of each key half: waves with qh = 1 hand their sums
+  // to the waves with qh = 0 through LDS (the Q / dO area is free now)
+  __syncthreads();
+  static_assert(sizeof(float) * 2 * 2 * NTD * 16 * 64 <= sizeof(__bf16) * 2 * BR * D, "reduction fits in q and g");
+  float* red = reinterpret_cast<float*>(&sm) + kh * (2 * NTD * 16 * 64);
+  if (qh == 1) {
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        red[(n * 16 + a) * 64 + lane] = dk[n][a];
+        red[((NTD + n) * 16 + a) * 64 + lane] = dv[n][a];
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && key_in) {
+    __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
+    __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        dk[n][a] += red[(n * 16 + a) * 64 + lane];
+        dv[n][a] += red[((NTD + n) * 16 + a) * 64 + lane];
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dcol = 32 * n + 8 * q4 + 4 * hi;
+        store4(dkp + dcol, dk[n], q4, p.scale);
+        store4(dvp + dcol, dv[n], q4, 1.0f);
+      }
+    }
+  }
+#endif
+}
+
+template <int D>
+struct DqSmem {
+  __bf16 k[BC * D];
+  __bf16 v[BC * D];
+};
+
+// One work-group per (batch, query head, query tile); wave w owns rows
+// 32 w .. 32 w + 31 of the tile, one row per lane (split over l and l + 32).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KS = D / 16;
+  constexpr int NTD = D / 32;
+  __shared__ DqSmem<D> sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int t = blockIdx.x % p.Tr;
+  const int bh = blockIdx.x / p.Tr;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int g = h / (p.Hq / p.Hkv);
+  const float c2 = p.scale * kLog2e;
+
+  const int row = t * BR + wave * 32 + l32;
+  const bool row_ok = row < p.Nq;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)row * p.qs_t + (int64_t)h * p.qs_h;
+  const __bf16* grow =
+      static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)row * p.dos_t + (int64_t)h * p.dos_h;
+  bf16x8 qf[KS], gf[KS];  // B operands: X[row][16 ks + 8 hi + 0..7]
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hi) : bf16x8{};
+    gf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(grow + 16 * ks + 8 * hi) : bf16x8{};
+  }
+  const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + row;
+  const float lse2 = row_ok ? p.lse[ri] * kLog2e : 0.0f;
+  const float dvr = row_ok ? p.dvec[ri] : 0.0f;
+
+  // visited blocks: the tile's CSR list (or every block), minus blocks wholly
+  // above the diagonal, exactly as the forward visits them
+  const int last_row = min(t * BR + BR, p.Nq) - 1;
+  int e0 = p.row_ptr ? p.row_ptr[t] : 0;
+  int e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
+  if (CAUSAL) {
+    if (p.row_ptr) {
+      while (e1 > e0 && p.col_idx[e1 - 1] * BC > last_row) --e1;
+    } else {
+      e1 = min(e1, last_row / BC + 1);
+    }
+  }
+  e0 = __builtin_amdgcn_readfirstlane(e0);
+  e1 = __builtin_amdgcn_readfirstlane(e1);
+
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
+  f32x16 dq[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
+
+  for (int e = e0; e < e1; ++e) {
+    const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
+    const int nkeys = min(BC, p.Nk - j * BC);
+    __syncthreads();
+    stage_tile<D, BC>(sm.k, kbase + (int64_t)(j * BC) * p.ks_t, p.ks_t, nkeys, tid);
+    stage_tile<D, BC>(sm.v, vbase + (int64_t)(j * BC) * p.vs_t, p.vs_t, nkeys, tid);
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(read_row<D>(sm.k, 32 * mt + l32, ks, hi), qf[ks], s);   // S^T[key][q]
+        dp = mfma32(read_row<D>(sm.v, 32 * mt + l32, ks, hi), gf[ks], dp);  // dP^T[key][q]
+      }
+      float dsv[16];
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = j * BC + 32 * mt + 8 * (a >> 2) + 4 * hi + (a & 3);
+        const bool ok = row_ok && key < p.n_valid && (!CAUSAL || key <= row);
+        const float pr = ok ? fast_exp2(fmaf(s[a], c2, -lse2)) : 0.0f;
+        dsv[a] = pr * (dp[a] - dvr);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 db = to_bf16x8(dsv + 8 * kk);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) dq[n] = mfma32(read_tr<D>(sm.k, 32 * mt + 16 * kk, n, lane), db, dq[n]);
+      }
+    }
+  }
+
+  if (row_ok) {
+    __bf16* dqp = static_cast<__bf16*>(p.dq) + (int64_t)b * p.dqs_b + (int64_t)row * p.dqs_t + (int64_t)h * p.dqs_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) store4(dqp + 32 * n + 8 * q4 + 4 * hi, dq[n], q4, p.scale);
+  }
+#endif
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  const int64_t dot_blocks = (rows * (D / 8) + NT - 1) / NT;
+  hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)dot_blocks), dim3(NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.Tc)), dim3(NT), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_prefill_bwd(const BwdParams& p, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.d == 64) return p.causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+  return p.causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+}
+
+}  // namespace bsattn

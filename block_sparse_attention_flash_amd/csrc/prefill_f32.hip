@@ -124,6 +124,7 @@ __global__ __launch_bounds__(BR) void prefill_f32_kernel(const PrefillParams p) 
     float* op = static_cast<float*>(p.out) + (int64_t)b * p.os_b + (int64_t)row * p.os_t + (int64_t)h * p.os_h;
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     for (int c = 0; c < D; ++c) op[c] = o[c] * inv;
+    if (p.lse) p.lse[((int64_t)b * p.Hq + h) * p.Nq + row] = l > 0.0f ? m_run + logf(l) : kNegInf;
   }
   if (p.tile_counters && tid == 0) {
     int32_t* tc = p.tile_counters + 2 * ((((int64_t)b * p.Hq + h) * p.Tr) + t);

@@ -122,6 +122,14 @@ bsattn_status bsattn_build_block_index(const bsattn_mask_spec* spec, int32_t n_q
 bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t* col_idx,
                                           int32_t Tr, int32_t Tc);
 
+/* Transpose of a host CSR (tiles -> key blocks) into its CSC (key blocks ->
+ * tiles): col_ptr [Tc + 1], row_idx [nnz], each key block's tiles in
+ * ascending order.  The backward pass walks it to find the query tiles that
+ * attended a key block.  Validates the CSR first (errors as
+ * bsattn_validate_block_index).  Host buffers. */
+bsattn_status bsattn_transpose_block_index(const int32_t* row_ptr, const int32_t* col_idx, int32_t Tr, int32_t Tc,
+                                           int32_t* col_ptr, int32_t* row_idx);
+
 /* Longest-first launch order for the tiles of a CSR (DiT article section 5.3
  * point 3: uneven rows unbalance the GPU): order[k] is the tile launched
  * k-th; ties keep ascending tile index.  Host buffers. */
@@ -200,6 +208,9 @@ typedef struct {
                                   the counters at zero again.  Calls that share a workspace
                                   must not overlap (same stream, or ordered by events). */
   size_t workspace_bytes;
+  float* lse;             /* optional device [B, Hq, Nq] float32: each row's natural-log sum of
+                             exp(scale q.k) over the keys it attended (-inf for a row with none),
+                             the statistic the backward pass (bsattn_prefill_bwd) rebuilds P from */
 } bsattn_prefill_args;
 
 /* Workspace bytes for a prefill whose schedule has n_slots partial slots. */
@@ -213,6 +224,74 @@ size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n
  * token stride x 2 bytes below 4 GiB (32-bit offsets within one head,
  * else BSATTN_ERR_UNSUPPORTED).  Returns BSATTN_ERR_HIP if the launch fails. */
 bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* prefill backward (static block mask)                                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Gradients of the static block-sparse attention computed by
+ * bsattn_prefill_fwd with lambda = 0: for the loss sum(out * dout),
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
+ *   P = the forward's softmax over each row's attended keys (rebuilt from
+ *       q, k and the forward's lse), dP = dout V^T,
+ *   dS = P * (dP - rowsum(dout * out))
+ * over the same token mask as the forward: blocks of the tile's CSR list (or
+ * every block), keys < n_valid, and key <= query when causal (blocks wholly
+ * above the diagonal are not visited).  With GQA, dk and dv of a K/V head
+ * sum its query heads.  The pages give no backward; this is the chain rule
+ * applied to the forward's definition (the DiT article trains with the
+ * block-sparse forward, section 4).  Every element of dq, dk, dv (rows < Nq,
+ * keys < Nk) is written; keys or rows that attend nothing get zeros.
+ *
+ * Three launches on `stream`: rowsum(dout * out) into the workspace, dk/dv
+ * (one work-group per batch, K/V head and 64-key block, walking the CSC over
+ * the group's query heads), dq (one work-group per batch, head and 128-row
+ * tile, walking the CSR).  No atomics: results are deterministic.
+ */
+typedef struct {
+  int32_t dtype;          /* BSATTN_BF16 */
+  const void* q;          /* device [B, Nq, Hq, d] bf16, as given to the forward */
+  const void* k;          /* device [B, Nk, Hkv, d] */
+  const void* v;          /* device [B, Nk, Hkv, d] */
+  const void* out;        /* device [B, Nq, Hq, d]: the forward's output */
+  const void* dout;       /* device [B, Nq, Hq, d]: gradient of the loss w.r.t. out */
+  const float* lse;       /* device [B, Hq, Nq]: the forward's lse output */
+  void* dq;               /* device [B, Nq, Hq, d] bf16 output */
+  void* dk;               /* device [B, Nk, Hkv, d] bf16 output */
+  void* dv;               /* device [B, Nk, Hkv, d] bf16 output */
+  int32_t B, Hq, Hkv, Nq, Nk, d; /* d in {64, 128}; Hq % Hkv == 0 */
+  int64_t q_stride[3];    /* element strides for batch, token, head (d contiguous), per tensor */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t do_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  const int32_t* row_ptr; /* device CSR at (128, 64) as in the forward, or NULL (every block) */
+  const int32_t* col_idx;
+  const int32_t* col_ptr; /* device transpose of that CSR (bsattn_transpose_block_index),
+                             required with it, NULL without */
+  const int32_t* row_idx;
+  int32_t n_valid;        /* as in the forward; 0 means Nk */
+  float scale;            /* as in the forward */
+  int32_t causal;         /* as in the forward; requires Nq == Nk */
+  int32_t Br, Bc;         /* 128, 64 */
+  void* workspace;        /* device, >= bsattn_prefill_bwd_workspace_size(B, Hq, Nq) bytes,
+                             256-byte aligned; no initial contents needed */
+  size_t workspace_bytes;
+} bsattn_prefill_bwd_args;
+
+/* Workspace bytes of a backward call (one float per query row and head). */
+size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Nq);
+
+/* Enqueue the backward on `stream`.  Validation as for the forward (pointers
+ * non-null and 16-byte aligned, strides multiples of 8 elements, d
+ * contiguous), plus: CSR and CSC both given or both NULL, lse non-NULL.
+ * The CSR and CSC contents are not read on the host.  BSATTN_ERR_HIP if a
+ * launch fails. */
+bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* decode (one new query token per sequence, split-KV + combine)              */

@@ -76,6 +76,47 @@ BAD_PREFILL = [
 ]
 
 
+def _good_bwd():
+    a = _abi.BwdArgs()
+    a.dtype = _abi.BSATTN_BF16
+    a.q = a.k = a.v = a.out = a.dout = a.dq = a.dk = a.dv = FAKE
+    a.lse = FAKE
+    a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d = 2, 8, 2, 256, 256, 128
+    for fld, h in (("q_stride", 8), ("k_stride", 2), ("v_stride", 2), ("o_stride", 8), ("do_stride", 8),
+                   ("dq_stride", 8), ("dk_stride", 2), ("dv_stride", 2)):
+        getattr(a, fld)[:] = [256 * h * 128, h * 128, 128]
+    a.scale, a.Br, a.Bc = 0.088, 128, 64
+    a.workspace = 0x100000
+    a.workspace_bytes = bsa.prefill_bwd_workspace_size(2, 8, 256)
+    return a
+
+
+BAD_BWD = [
+    ("fp32", lambda a: setattr(a, "dtype", _abi.BSATTN_FP32), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("null dout", lambda a: setattr(a, "dout", None), _abi.BSATTN_ERR_INVALID_ARG),
+    ("misaligned dk", lambda a: setattr(a, "dk", FAKE + 8), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("null lse", lambda a: setattr(a, "lse", None), _abi.BSATTN_ERR_INVALID_ARG),
+    ("Hq % Hkv", lambda a: setattr(a, "Hkv", 3), _abi.BSATTN_ERR_INVALID_ARG),
+    ("d = 96", lambda a: setattr(a, "d", 96), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("dq stride not x8", lambda a: a.dq_stride.__setitem__(1, 8 * 128 + 4), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("CSR without CSC", lambda a: (setattr(a, "row_ptr", FAKE), setattr(a, "col_idx", FAKE)),
+     _abi.BSATTN_ERR_INVALID_ARG),
+    ("causal Nq != Nk", lambda a: (setattr(a, "causal", 1), setattr(a, "Nk", 128)), _abi.BSATTN_ERR_INVALID_ARG),
+    ("n_valid > Nk", lambda a: setattr(a, "n_valid", 257), _abi.BSATTN_ERR_INVALID_ARG),
+    ("Br 64", lambda a: setattr(a, "Br", 64), _abi.BSATTN_ERR_UNSUPPORTED),
+    ("workspace small", lambda a: setattr(a, "workspace_bytes", 64), _abi.BSATTN_ERR_CAPACITY),
+    ("workspace misaligned", lambda a: setattr(a, "workspace", 0x100010), _abi.BSATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", BAD_BWD, ids=[b[0] for b in BAD_BWD])
+def test_backward_rejects(name, mutate, status):
+    a = _good_bwd()
+    mutate(a)
+    st = bsa.library().bsattn_prefill_bwd(C.byref(a), None)
+    assert st == status, (name, bsa.library().bsattn_last_error())
+
+
 @pytest.mark.parametrize("name,mutate,status", BAD_PREFILL, ids=[b[0] for b in BAD_PREFILL])
 def test_prefill_rejects(name, mutate, status):
     a = _good_prefill()

@@ -175,3 +175,22 @@ def test_schedule_validation():
     assert bsa.prefill_workspace_size(2, 16, 64, 3) >= 3 * 2 * 16 * (128 * 66 * 4 + 3 * 4)
     a.n_merges, a.n_slots = 4, 2                                   # more merges than slots
     assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG
+
+
+def test_transpose_block_index():
+    """CSC of a CSR: every (tile, block) pair exactly once, tiles ascending per
+    block; empty tiles and never-kept blocks; malformed CSRs are refused."""
+    g = np.random.default_rng(5)
+    for Tr, Tc in ((1, 1), (3, 5), (34, 68), (7, 2)):
+        tm = g.random((Tr, Tc)) < 0.4
+        tm[0] = False
+        row_ptr = np.concatenate([[0], np.cumsum(tm.sum(axis=1))]).astype(np.int32)
+        col_idx = np.concatenate([np.nonzero(r)[0] for r in tm] + [np.zeros(0, int)]).astype(np.int32)
+        col_ptr, row_idx = bsa.transpose_block_index(row_ptr, col_idx, Tc)
+        assert col_ptr[0] == 0 and col_ptr[-1] == tm.sum()
+        for j in range(Tc):
+            assert row_idx[col_ptr[j]:col_ptr[j + 1]].tolist() == np.nonzero(tm[:, j])[0].tolist()
+    with pytest.raises(bsa.BsattnError):
+        bsa.transpose_block_index(np.array([0, 2], np.int32), np.array([1, 0], np.int32), 4)   # not ascending
+    with pytest.raises(bsa.BsattnError):
+        bsa.transpose_block_index(np.array([0, 1], np.int32), np.array([4], np.int32), 4)      # out of range

@@ -1,0 +1,175 @@
+"""GPU parity of bsattn_prefill_bwd (and the forward's lse output) against the
+float64 gradient oracle, through the C ABI.
+
+Tolerance (the pages fix none for gradients; derived from the arithmetic):
+the kernels multiply exact bf16 inputs in fp32 but round P and dS to bf16
+(relative error <= 2^-9 each) before the dV, dK and dQ products, take
+rowsum(dO * O) from the forward's bf16-rounded output, and round the
+gradients to bf16 (2^-9 relative).  Each gradient element is a sum of many
+such terms with independent roundings, so its error is a few 2^-9 of the
+size of its terms; against the scale of the gradient, s = max |reference|
+of the tensor, the test asks max-abs <= 2^-6 s and mean-abs <= 2^-9 s.
+lse = m + ln(l) comes from the forward, whose row sum l adds the P values
+the P.V product uses; at d = 64 those are the bf16-rounded P (relative error
+<= 2^-9 per term, so <= 2^-9 on l and on ln l), at d = 128 fp32 P: max-abs
+<= 2^-9 + 1e-4.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flash_amd as bsa
+from oracle import backward as BW
+from oracle import masks as M
+from workloads import gen_prefill_grad_output, gen_prefill_inputs, get_config
+from workloads.configs import PrefillWorkload, dit_image_text_spec
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MAX_REL, MEAN_REL, LSE_ABS = 2.0 ** -6, 2.0 ** -9, 2.0 ** -9 + 1e-4
+
+
+def _say(msg):
+    print(f"[gpu-backward] {msg}", file=sys.stderr, flush=True)
+
+
+def _cfg(N=300, d=128, Hq=4, Hkv=2, seed=201, generator="iid", causal=False, mask=None):
+    return PrefillWorkload(name="bwd", description="", dtype="bf16", B=2, Hq=Hq, Hkv=Hkv, N=N, d=d, Br=128, Bc=64,
+                           causal=causal, lam=0.0, mask=mask, seed=seed, generator=generator)
+
+
+def run_fwd_bwd(cfg, q, k, v, dout, csr=None, n_valid=None):
+    """Forward (with lse) then backward on the GPU; host copies of everything."""
+    B, N, Hq, d = q.shape
+    Tc = -(-N // 64)
+    rp = ci = cp = ri = None
+    if csr is not None:
+        colp, rowi = bsa.transpose_block_index(csr[0], csr[1], Tc)
+        rp, ci = torch.from_numpy(csr[0]).to(DEV), torch.from_numpy(csr[1]).to(DEV)
+        cp, ri = torch.from_numpy(colp).to(DEV), torch.from_numpy(rowi).to(DEV)
+    nv = cfg.n_valid if n_valid is None else n_valid
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=DEV)
+    out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, row_ptr=rp, col_idx=ci, n_valid=nv, lse=lse)
+    dq, dk, dv = bsa.prefill_bwd(q, k, v, out, dout, lse, scale=cfg.scale, causal=cfg.causal, row_ptr=rp,
+                                 col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=nv)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu().numpy(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def token_mask(N, csr, n_valid, causal):
+    Tr, Tc = -(-N // 128), -(-N // 64)
+    tm = np.ones((Tr, Tc), bool)
+    if csr is not None:
+        tm[:] = False
+        for t in range(Tr):
+            tm[t, csr[1][csr[0][t]:csr[0][t + 1]]] = True
+    return M.expand_token_mask(tm, N, N, 128, 64, n_valid, causal)
+
+
+def compare_grad(got, ref, what):
+    got = np.asarray(got.float().numpy(), dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    s = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(got - ref)
+    _say(f"  {what}: scale {s:.3e}, max-abs {err.max():.3e} ({err.max() / s:.2e} s), "
+         f"mean-abs {err.mean():.3e} ({err.mean() / s:.2e} s)")
+    assert err.max() <= MAX_REL * s, f"{what}: max-abs {err.max():.3e} > {MAX_REL * s:.3e}"
+    assert err.mean() <= MEAN_REL * s, f"{what}: mean-abs {err.mean():.3e} > {MEAN_REL * s:.3e}"
+
+
+def check_all(cfg, q, k, v, dout, csr=None, n_valid=None):
+    nv = cfg.n_valid if n_valid is None else n_valid
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr, nv)
+    mask = token_mask(cfg.N, csr, nv, cfg.causal)
+    rq, rk, rv = BW.prefill_grads(q, k, v, dout, mask, cfg.scale)
+    rl = BW.prefill_lse(q, k, mask, cfg.scale)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), fin), "lse: rows with and without attended keys differ"
+    assert np.abs(lse[fin] - rl[fin]).max() <= LSE_ABS, f"lse max-abs {np.abs(lse[fin] - rl[fin]).max():.3e}"
+    compare_grad(dq, rq, "dq")
+    compare_grad(dk, rk, "dk")
+    compare_grad(dv, rv, "dv")
+    # structural zeros: keys nobody attends, rows that attend nothing
+    dead_k = ~mask.any(axis=0)
+    dead_q = ~mask.any(axis=1)
+    assert torch.all(dk[:, torch.from_numpy(dead_k)] == 0) and torch.all(dv[:, torch.from_numpy(dead_k)] == 0)
+    assert torch.all(dq[:, torch.from_numpy(dead_q)] == 0)
+
+
+def _random_csr(Tr, Tc, seed):
+    """A random tile mask with one empty tile row and one key block no tile keeps."""
+    g = np.random.default_rng(seed)
+    tm = g.random((Tr, Tc)) < 0.55
+    tm[1] = False
+    tm[:, 2] = False
+    tm[0, 0] = tm[2, 4] = True
+    row_ptr = np.concatenate([[0], np.cumsum(tm.sum(axis=1))]).astype(np.int32)
+    col_idx = np.concatenate([np.nonzero(r)[0] for r in tm]).astype(np.int32)
+    return row_ptr, col_idx
+
+
+CASES = ["dense", "causal", "csr", "csr_causal_nvalid"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES)
+def test_backward_small(case, d):
+    """N = 300 (three query tiles with a ragged last one, five key blocks),
+    GQA with two query heads per K/V head."""
+    causal = "causal" in case
+    n_valid = 280 if "nvalid" in case else 300
+    cfg = _cfg(d=d, causal=causal, seed=201 + d)
+    _say(f"backward {case} d{d} N300 Hq4 Hkv2 n_valid {n_valid}")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    csr = _random_csr(3, 5, 7 + d) if "csr" in case else None
+    check_all(cfg, q, k, v, dout, csr, n_valid)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_dit_mask(d):
+    """The DiT image+text mask family (2-D window, text segment, anchors) at a
+    reduced size, per-head offsets (cfg2's recipe), padding keys past n_valid."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13
+    cfg = _cfg(N=n, d=d, Hq=4, Hkv=4, generator="iid_offset", seed=211, mask=spec)
+    _say(f"backward DiT mask N{n} d{d}")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    check_all(cfg, q, k, v, dout, csr)
+
+
+def test_backward_deterministic():
+    cfg = _cfg(N=700, d=128, Hq=8, Hkv=2, seed=221, causal=True)
+    _say("backward determinism")
+    q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+    dout = gen_prefill_grad_output(cfg).to(DEV)
+    a = run_fwd_bwd(cfg, q, k, v, dout)
+    b = run_fwd_bwd(cfg, q, k, v, dout)
+    for x, y in zip(a[2:], b[2:]):
+        assert torch.equal(x, y)
+
+
+def test_backward_cfg2_full_size_sampled():
+    """The DiT image+text workload at full size (B 2, H 16, N 4352, d 64):
+    every gradient of two (batch, head) pairs against the oracle run on that
+    head alone (dK and dV of a head depend only on that head when Hq = Hkv)."""
+    cfg = get_config("cfg2")
+    _say("backward cfg2 full size, heads (0, 3) and (1, 12)")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr)
+    mask = token_mask(cfg.N, csr, cfg.n_valid, False)
+    for b, h in ((0, 3), (1, 12)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        rq, rk, rv = BW.prefill_grads(sl(q), sl(k), sl(v), sl(dout), mask, cfg.scale)
+        compare_grad(sl(dq), rq, f"dq b{b} h{h}")
+        compare_grad(sl(dk), rk, f"dk b{b} h{h}")
+        compare_grad(sl(dv), rv, f"dv b{b} h{h}")
+        rl = BW.prefill_lse(sl(q), sl(k), mask, cfg.scale)[0, 0]
+        assert np.abs(lse[b, h] - rl).max() <= LSE_ABS

@@ -13,6 +13,6 @@ from .configs import (  # noqa: F401
     CONFIGS, get_config,
 )
 from .generate import (  # noqa: F401
-    sinusoidal_position, gen_prefill_inputs, gen_decode_inputs,
+    sinusoidal_position, gen_prefill_inputs, gen_prefill_grad_output, gen_decode_inputs,
     gen_decode_sequence,
 )

@@ -35,7 +35,7 @@ import torch
 
 from .configs import DecodeWorkload, PrefillWorkload
 
-_TAG_Q, _TAG_K, _TAG_V, _TAG_OFF = 1, 2, 3, 4
+_TAG_Q, _TAG_K, _TAG_V, _TAG_OFF, _TAG_DO = 1, 2, 3, 4, 5
 
 
 def _gen(seed: int, tag: int, sub: int, device) -> torch.Generator:
@@ -106,6 +106,15 @@ def gen_prefill_inputs(cfg: PrefillWorkload, device="cpu", B=None, N=None):
         raise ValueError(cfg.generator)
     dt = _store_dtype(cfg)
     return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def gen_prefill_grad_output(cfg: PrefillWorkload, device="cpu", B=None, N=None):
+    """Gradient of the loss w.r.t. the prefill output, dO [B, N, Hq, d]:
+    i.i.d. N(0, 1), rounded to the storage dtype (the backward's input)."""
+    B = cfg.B if B is None else B
+    N = cfg.N if N is None else N
+    g = _randn((B, N, cfg.Hq, cfg.d), cfg.seed, _TAG_DO, 0, torch.device(device))
+    return g.to(_store_dtype(cfg)).contiguous()
 
 
 def gen_decode_sequence(cfg: DecodeWorkload, b: int, device="cpu", L=None):
