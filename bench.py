@@ -191,6 +191,67 @@ def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool =
     return res
 
 
+# ---------------------------------------------------------------------------- backward
+
+def visited_pairs(cfg, rp_h, ci_h):
+    """(query tile, key block) pairs the forward and backward visit, per (batch, head)."""
+    Tr, Tc = -(-cfg.N // cfg.Br), -(-cfg.N // cfg.Bc)
+    n = 0
+    for t in range(Tr):
+        blocks = range(Tc) if rp_h is None else ci_h[rp_h[t]:rp_h[t + 1]]
+        last = min((t + 1) * cfg.Br, cfg.N) - 1
+        n += sum(1 for j in blocks if not cfg.causal or j * cfg.Bc <= last)
+    return n
+
+
+def run_backward_workload(name: str, steps: int, warmup: int):
+    """The static block-sparse backward (dot, dK/dV, dQ kernels) on a prefill
+    workload at lambda = 0, with the forward timed alongside.  Processed
+    FLOPs: the dK/dV kernel computes S, dP, dV, dK (4 products) and the dQ
+    kernel S, dP, dQ (3) per visited (tile, block) pair of every head, each
+    2 Br Bc d; the usual accounting of a backward counts 5 (S and dP once)."""
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    from workloads import get_config, gen_prefill_inputs, gen_prefill_grad_output
+
+    cfg = get_config(name)
+    dev = "cuda"
+    log(f"backward {name}: generating inputs ({cfg.description})")
+    q, k, v = gen_prefill_inputs(cfg, device=dev)
+    dout = gen_prefill_grad_output(cfg, device=dev)
+    Tc = -(-cfg.N // cfg.Bc)
+    rp = ci = cp = ri = rp_h = ci_h = None
+    if cfg.mask is not None:
+        rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
+        cp_h, ri_h = bsa.transpose_block_index(rp_h, ci_h, Tc)
+        rp, ci, cp, ri = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, cp_h, ri_h))
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    fwd = bsa.prefill_plan(q, k, v, scale=cfg.scale, causal=cfg.causal, row_ptr=rp, col_idx=ci,
+                           n_valid=cfg.n_valid, out=out, lse=lse)
+    fwd()
+    bwd = bsa.prefill_bwd_plan(q, k, v, out, dout, lse, scale=cfg.scale, causal=cfg.causal, row_ptr=rp,
+                               col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=cfg.n_valid)
+    torch.cuda.synchronize()
+    pairs = visited_pairs(cfg, rp_h, ci_h) * cfg.B * cfg.Hq
+    per_gemm = 2 * cfg.Br * cfg.Bc * cfg.d
+    log(f"backward {name}: timing {steps} steps")
+    tb = time_launches(bwd, steps, warmup)
+    tf = time_launches(fwd, steps, warmup)
+    ms = tb["ms_per_step"]
+    res = {"workload": name, "description": cfg.description, "ms_per_step": ms, "timing": tb,
+           "forward_ms_per_step": tf["ms_per_step"], "backward_over_forward": ms / tf["ms_per_step"],
+           "visited_pairs": pairs,
+           "processed_tflops": 7 * per_gemm * pairs / (ms * 1e-3) / 1e12,
+           "standard_5gemm_tflops": 5 * per_gemm * pairs / (ms * 1e-3) / 1e12,
+           "frac_of_bf16_peak_processed": 7 * per_gemm * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    log(f"backward {name}: {ms:.4f} ms ({res['backward_over_forward']:.2f}x forward), "
+        f"{res['processed_tflops']:.0f} processed TFLOP/s, {res['standard_5gemm_tflops']:.0f} standard")
+    del q, k, v, dout, out, lse, fwd, bwd
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------- decode
 
 def run_decode_workload(name: str, steps: int, warmup: int):
@@ -508,6 +569,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the metric line: a lambda sweep (static + dynamic skipping together) per "
                          "workload, as one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the metric line: the static block-sparse backward on the prefill workloads")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the metric line: the decode order and decision variants on the decode workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -540,6 +603,11 @@ def main(argv=None) -> int:
         cal = calibration_demo()
         print(json.dumps({"sweep": rep, "decode_variants": var, "calibration": cal, "steps": a.steps,
                           "device": torch.cuda.get_device_name(0)}))
+        return 0
+    if a.backward:
+        names = [a.workload] + [n for n in (a.also.split(",") if a.also and not a.no_also else []) if n != "cfg5"]
+        rep = [run_backward_workload(n, a.steps, a.warmup) for n in names]
+        print(json.dumps({"backward": rep, "device": torch.cuda.get_device_name(0)}))
         return 0
     if a.variants:
         var = decode_variants("cfg5", [40.0 / 131072, 1e-2, 0.1], min(a.steps, 50), min(a.warmup, 20))

@@ -39,7 +39,7 @@ from . import _abi
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
     "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace",
-    "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_workspace_size", "transpose_block_index",
+    "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_plan", "prefill_bwd_workspace_size", "transpose_block_index",
     "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits",
     "decode_split_blocks", "decode_check",
     "calibrate_fit", "calibrate", "decode_sparsity",
@@ -329,14 +329,11 @@ def prefill_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
     return int(library().bsattn_prefill_bwd_workspace_size(B, Hq, Nq))
 
 
-def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
-                row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
-                dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Gradients of the static block-sparse forward (lambda = 0) for the loss
-    sum(out * dout): q, out, dout [B, Nq, Hq, d], k, v [B, Nk, Hkv, d] bf16,
-    ``lse`` float32 [B, Hq, Nq] from ``prefill_fwd(..., lse=)``.  The mask
-    arguments are the forward's; with a CSR, ``col_ptr``/``row_idx`` are the
-    device copies of ``transpose_block_index``.  Returns (dq, dk, dv)."""
+def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
+                     row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
+                     dq=None, dk=None, dv=None, workspace=None) -> Plan:
+    """Marshal a backward (arguments as ``prefill_bwd``) into a reusable Plan
+    whose call returns (dq, dk, dv)."""
     torch = _torch()
     if q.dtype != torch.bfloat16:
         raise BsattnError(_abi.BSATTN_ERR_UNSUPPORTED, "the backward is implemented for bf16")
@@ -364,8 +361,23 @@ def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causa
     a.Br, a.Bc = 128, 64
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
-    _check(library().bsattn_prefill_bwd(C.byref(a), C.c_void_p(_stream_handle(stream))))
-    return dq, dk, dv
+    keep = (q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx, workspace)
+    return Plan(library().bsattn_prefill_bwd, a, (dq, dk, dv), keep)
+
+
+def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
+                row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the static block-sparse forward (lambda = 0) for the loss
+    sum(out * dout): q, out, dout [B, Nq, Hq, d], k, v [B, Nk, Hkv, d] bf16,
+    ``lse`` float32 [B, Hq, Nq] from ``prefill_fwd(..., lse=)``.  The mask
+    arguments are the forward's; with a CSR, ``col_ptr``/``row_idx`` are the
+    device copies of ``transpose_block_index``.  ``workspace`` (uint8, at
+    least ``prefill_bwd_workspace_size`` bytes) is allocated here if None.
+    Returns (dq, dk, dv)."""
+    return prefill_bwd_plan(q, k, v, out, dout, lse, scale=scale, causal=causal, row_ptr=row_ptr,
+                            col_idx=col_idx, col_ptr=col_ptr, row_idx=row_idx, n_valid=n_valid, dq=dq, dk=dk,
+                            dv=dv, workspace=workspace)(stream)
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:

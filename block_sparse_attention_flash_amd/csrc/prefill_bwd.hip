@@ -40,40 +40,50 @@ constexpr int BC = 64;
 constexpr int NT = 256;
 
 // R x D bf16 tile in LDS read both row-wise (16-byte chunks: MFMA operand
-// rows) and transposed (ds_read_b64_tr_b16 over 8 rows x 4 chunks).  Chunk c
-// of row r sits at r * CH + (c ^ swz(r)).  swz depends on r % 8 only, so a
-// transposed read 8 or 16 rows further down keeps its pattern; the 4 rows
-// of a transposed read fall into 4 different 64-byte bank groups, and 16
-// consecutive rows of a row read use 8 different chunks (a 2-way conflict).
+// rows) and transposed (ds_read_b64_tr_b16 over 4 rows x 4 chunks per
+// instruction).  Chunk c of row r sits at r * CH + (c ^ swz(r)), swz a
+// bijection of r % 16 (d = 128) or of (r / 2) % 8 (d = 64, two rows per
+// 256-byte bank line) chosen so that both patterns touch every bank once:
+//   row reads: 16 consecutive rows, one chunk each -> 16 (8 per row parity
+//              at d = 64) different chunk positions;
+//   transposed reads: 4 consecutive rows, 4 chunks of one 64-byte group each
+//              -> the rows land in 4 different 64-byte groups (bits 2-3 of
+//              swz; at d = 64 rows r and r + 2 differ in bit 2, rows r and
+//              r + 1 already sit in different halves of the line).
 template <int D>
 struct BTile {
   static constexpr int CH = D / 8;
   __device__ static __forceinline__ int swz(int r) {
-    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 1) : 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1);
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
   __device__ static __forceinline__ int pos(int r, int c) { return (r * CH + (c ^ swz(r))) * 8; }
 };
 
-// Copy rows [0, nrows) of a R x D global tile (row stride in elements) into
-// LDS; rows >= nrows are zero-filled.
+// A R x D global tile staged through registers: load() issues the global
+// reads of rows [0, nrows) (rows >= nrows read as zeros) one tile ahead,
+// store() writes them to LDS once the tile there is no longer read.
 template <int D, int R>
-__device__ __forceinline__ void stage_tile(__bf16* tile, const __bf16* src, int64_t stride, int nrows, int tid) {
-  constexpr int CH = D / 8;
-  constexpr int PER = R * CH / NT;
+struct Staged {
+  static constexpr int CH = D / 8;
+  static constexpr int PER = R * CH / NT;
   bf16x8 v[PER];
+  __device__ __forceinline__ void load(const __bf16* src, int64_t stride, int nrows, int tid) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int x = i * NT + tid;
-    const int r = x / CH, c = x % CH;
-    v[i] = r < nrows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * stride + 8 * c) : bf16x8{};
+    for (int i = 0; i < PER; ++i) {
+      const int x = i * NT + tid;
+      const int r = x / CH, c = x % CH;
+      v[i] = r < nrows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * stride + 8 * c) : bf16x8{};
+    }
   }
+  __device__ __forceinline__ void store(__bf16* tile, int tid) const {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int x = i * NT + tid;
-    const int r = x / CH, c = x % CH;
-    *reinterpret_cast<bf16x8*>(tile + BTile<D>::pos(r, c)) = v[i];
+    for (int i = 0; i < PER; ++i) {
+      const int x = i * NT + tid;
+      const int r = x / CH, c = x % CH;
+      *reinterpret_cast<bf16x8*>(tile + BTile<D>::pos(r, c)) = v[i];
+    }
   }
-}
+};
 
 // Row fragment: X[r][16 ks + 8 hi + 0..7] (A operand rows, or B operand columns).
 template <int D>
@@ -125,22 +135,54 @@ __device__ __forceinline__ void store4(__bf16* dst, const f32x16& acc, int q4, f
   *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v4, bf16x4);
 }
 
+// Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle; range checking against num_records).
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global -> LDS DMA of a 64 x D tile (buffer_load_dwordx4 ... lds).  The
+// descriptor's range ends at the tensor's last row of this (batch, head), so
+// rows past it read as zeros.  Instruction i of wave w lands lane l's 16 bytes
+// at LDS chunk slot (4 i + w) 64 + l; the lane fetches the global chunk whose
+// swizzled position is that slot (BTile::pos is a bijection on every row).
+template <int D>
+__device__ __forceinline__ void dma_tile64(__bf16* tile, const __bf16* head, int rows_total, int64_t stride_t,
+                                           int row0, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int NI = 64 * CH / NT;
+  const uint32_t extent = (uint32_t)(((int64_t)(rows_total - 1) * stride_t + D) * 2);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, (int)extent, kBufferWord3);
+  const uint32_t soff = (uint32_t)((int64_t)row0 * stride_t * 2);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (4 * i + wave) * 64 + lane;
+    const int r = slot / CH, cp = slot % CH;
+    const int c = cp ^ BTile<D>::swz(r);
+    const uint32_t voff = (uint32_t)(((int64_t)r * stride_t + 8 * c) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (4 * i + wave) * 64 * 8), 16, voff, soff, 0, 0);
+  }
+}
+
 template <int D>
 struct DkdvSmem {
-  __bf16 q[BR * D];
-  __bf16 g[BR * D];   // dout
-  float lse2[BR];     // lse in log2 units
-  float dv[BR];
+  __bf16 k[BC * D];   // the block's keys
+  __bf16 v[BC * D];
+  __bf16 q[64 * D];   // 64 query rows of the current tile (one stage)
+  __bf16 g[64 * D];   // their dout
+  float lse2[64];     // lse in log2 units
+  float dv[64];
 };
 
-// Work-groups per CU the dK/dV kernel's registers are cut for: at d = 128 the
-// K and V fragments (64 registers) and the dK and dV accumulators (128) leave
-// no room for a second group without spilling.
+// Work-groups per CU the dK/dV kernel is cut for: K and V stay in LDS and
+// query rows stream in 64-row stages, so two groups fit at d = 128 (64.5 KB
+// of LDS, at most 256 registers each) and three at d = 64.
 template <int D>
-constexpr int kDkdvBlocksPerCu = D == 64 ? 2 : 1;
+constexpr int kDkdvBlocksPerCu = D == 64 ? 3 : 2;
 
 // One work-group per (batch, K/V head, key block).  Wave w: keys 32 (w & 1)
-// .. +31 of the block (kh), query rows 64 (w >> 1) .. +63 of each tile (qh).
+// .. +31 of the block (kh), rows 32 (w >> 1) .. +31 of each 64-row stage (qh).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -151,24 +193,23 @@ __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  const int j = blockIdx.x % p.Tc;
-  const int bg = blockIdx.x / p.Tc;
+  // work order: key block major, ascending (under a causal mask the first
+  // blocks have the most query tiles: longest first); the (batch, K/V head)
+  // index runs fastest, so with B Hkv a multiple of 8 a group stays on one
+  // XCD (work-group i runs on XCD i % 8) and its Q / dO tiles in one L2
+  const int NBG = p.B * p.Hkv;
+  const int j = blockIdx.x / NBG;
+  const int bg = blockIdx.x % NBG;
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const int G = p.Hq / p.Hkv;
   const float c2 = p.scale * kLog2e;
 
-  // K and V rows of this lane's key as B operands: X[key][16 ks + 8 hi + 0..7]
-  const int key = j * BC + 32 * kh + l32;
-  const bool key_in = key < p.Nk;
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = key_in ? *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * p.ks_t + 16 * ks + 8 * hi) : bf16x8{};
-    vf[ks] = key_in ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * p.vs_t + 16 * ks + 8 * hi) : bf16x8{};
-  }
+  const int key = j * BC + 32 * kh + l32;  // this lane's key (column of S)
   const bool key_ok = key < p.n_valid;
+  dma_tile64<D>(sm.k, static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h, p.Nk, p.ks_t,
+                j * BC, wave, lane);
+  dma_tile64<D>(sm.v, static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h, p.Nk, p.vs_t,
+                j * BC, wave, lane);
 
   f32x16 dk[NTD], dv[NTD];
 #pragma unroll
@@ -191,60 +232,66 @@ __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const
   e1 = __builtin_amdgcn_readfirstlane(e1);
   const int ntile = e1 - e0;
 
-  for (int it = 0; it < G * ntile; ++it) {
-    const int hh = it / ntile;
-    const int e = e0 + it % ntile;
+  // work: (query head, tile, 64-row half) in order; halves past the last row
+  // or (causal) wholly above the block's first key are not visited
+  for (int it = 0; it < 2 * G * ntile; ++it) {
+    const int hf = it & 1;
+    const int e = e0 + (it >> 1) % ntile;
+    const int h = g * G + (it >> 1) / ntile;
     const int t = __builtin_amdgcn_readfirstlane(p.row_idx ? p.row_idx[e] : e);
-    if (CAUSAL && t * BR + BR - 1 < j * BC) continue;  // wholly above the diagonal: not visited
-    const int h = g * G + hh;
-    const int nrows = min(BR, p.Nq - t * BR);
-    __syncthreads();  // the previous tile's LDS reads are done
-    stage_tile<D, BR>(sm.q, static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)(t * BR) * p.qs_t +
-                                (int64_t)h * p.qs_h, p.qs_t, nrows, tid);
-    stage_tile<D, BR>(sm.g, static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b +
-                                (int64_t)(t * BR) * p.dos_t + (int64_t)h * p.dos_h, p.dos_t, nrows, tid);
-    if (tid < BR) {
-      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + t * BR + tid;
+    const int row0 = t * BR + 64 * hf;
+    if (row0 >= p.Nq || (CAUSAL && row0 + 63 < j * BC)) continue;
+    const int nrows = min(64, p.Nq - row0);
+    __syncthreads();  // every wave is done reading the previous stage
+    dma_tile64<D>(sm.q, static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h, p.Nq, p.qs_t,
+                  row0, wave, lane);
+    dma_tile64<D>(sm.g, static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h, p.Nq,
+                  p.dos_t, row0, wave, lane);
+    if (tid < 64) {
+      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + row0 + tid;
       sm.lse2[tid] = tid < nrows ? p.lse[ri] * kLog2e : 0.0f;
       sm.dv[tid] = tid < nrows ? p.dvec[ri] : 0.0f;
     }
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA has landed
+    __syncthreads();                                   // and every other wave's
 
-#pragma unroll 1
-    for (int c = 0; c < 2; ++c) {
-      const int r0 = qh * 64 + 32 * c;  // first tile row of this chunk
-      f32x16 s = f32x16{}, dp = f32x16{};
+    const int r0 = 32 * qh;  // first stage row of this wave's chunk
+    // S = Q K^T and dP = dO V^T, the fragments of one k-step at a time (the
+    // scheduling barriers keep the compiler from hoisting every LDS read,
+    // which would not fit two work-groups' registers)
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row<D>(sm.q, r0 + l32, ks, hi), kf[ks], s);   // S[q][key]
-        dp = mfma32(read_row<D>(sm.g, r0 + l32, ks, hi), vf[ks], dp);  // dP[q][key]
-      }
-      float pv[16], dsv[16];
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(read_row<D>(sm.q, r0 + l32, ks, hi), read_row<D>(sm.k, 32 * kh + l32, ks, hi), s);   // S[q][key]
+      dp = mfma32(read_row<D>(sm.g, r0 + l32, ks, hi), read_row<D>(sm.v, 32 * kh + l32, ks, hi), dp);  // dP[q][key]
+      if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
+    for (int kk = 0; kk < 2; ++kk) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int a = 8 * kk + i;
         const int rl = r0 + 8 * (a >> 2) + 4 * hi + (a & 3);
-        const int row = t * BR + rl;
-        const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row);
-        pv[a] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse2[rl])) : 0.0f;
-        dsv[a] = pv[a] * (dp[a] - sm.dv[rl]);
+        const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
+        pv[i] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse2[rl])) : 0.0f;
+        dsv[i] = pv[i] * (dp[a] - sm.dv[rl]);
       }
+      const bf16x8 pb = to_bf16x8(pv);
+      const bf16x8 db = to_bf16x8(dsv);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 pb = to_bf16x8(pv + 8 * kk);
-        const bf16x8 db = to_bf16x8(dsv + 8 * kk);
-#pragma unroll
-        for (int n = 0; n < NTD; ++n) {
-          dv[n] = mfma32(read_tr<D>(sm.g, r0 + 16 * kk, n, lane), pb, dv[n]);  // dV^T += dO^T P
-          dk[n] = mfma32(read_tr<D>(sm.q, r0 + 16 * kk, n, lane), db, dk[n]);  // dK^T += Q^T dS
-        }
+      for (int n = 0; n < NTD; ++n) {
+        dv[n] = mfma32(read_tr<D>(sm.g, r0 + 16 * kk, n, lane), pb, dv[n]);  // dV^T += dO^T P
+        dk[n] = mfma32(read_tr<D>(sm.q, r0 + 16 * kk, n, lane), db, dk[n]);  // dK^T += Q^T dS
+        if (n % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // the two query halves of each key half: waves with qh = 1 hand their sums
-  // to the waves with qh = 0 through LDS (the Q / dO area is free now)
+  // the two row halves of each key half: waves with qh = 1 hand their sums to
+  // the waves with qh = 0 through LDS (the Q / dO area is free now)
   __syncthreads();
-  static_assert(sizeof(float) * 2 * 2 * NTD * 16 * 64 <= sizeof(__bf16) * 2 * BR * D, "reduction fits in q and g");
+  static_assert(sizeof(float) * 2 * 2 * NTD * 16 * 64 <= sizeof(__bf16) * 4 * 64 * D, "reduction fits in k, v, q, g");
   float* red = reinterpret_cast<float*>(&sm) + kh * (2 * NTD * 16 * 64);
   if (qh == 1) {
 #pragma unroll
@@ -256,7 +303,7 @@ __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const
       }
   }
   __syncthreads();
-  if (qh == 0 && key_in) {
+  if (qh == 0 && key < p.Nk) {
     __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
     __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
 #pragma unroll
@@ -294,10 +341,17 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int t = blockIdx.x % p.Tr;
-  const int bh = blockIdx.x / p.Tr;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int g = h / (p.Hq / p.Hkv);
+  // work order: tile major (under a causal mask the last tiles, the longest,
+  // first), then the group's query heads, the (batch, K/V head) index
+  // fastest: with B Hkv a multiple of 8 a group stays on one XCD
+  const int G = p.Hq / p.Hkv;
+  const int NBG = p.B * p.Hkv;
+  const int bg = blockIdx.x % NBG;
+  const int hh = (blockIdx.x / NBG) % G;
+  const int rank = blockIdx.x / (NBG * G);
+  const int t = CAUSAL ? p.Tr - 1 - rank : rank;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int h = g * G + hh;
   const float c2 = p.scale * kLog2e;
 
   const int row = t * BR + wave * 32 + l32;
@@ -336,13 +390,22 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
 
-  for (int e = e0; e < e1; ++e) {
+  // the next block's K and V are read into registers while this one computes
+  Staged<D, BC> nk, nv;
+  auto fetch = [&](int e) __attribute__((always_inline)) {
     const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
     const int nkeys = min(BC, p.Nk - j * BC);
+    nk.load(kbase + (int64_t)(j * BC) * p.ks_t, p.ks_t, nkeys, tid);
+    nv.load(vbase + (int64_t)(j * BC) * p.vs_t, p.vs_t, nkeys, tid);
+  };
+  if (e0 < e1) fetch(e0);
+  for (int e = e0; e < e1; ++e) {
+    const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
+    __syncthreads();  // every wave is done reading the previous block
+    nk.store(sm.k, tid);
+    nv.store(sm.v, tid);
     __syncthreads();
-    stage_tile<D, BC>(sm.k, kbase + (int64_t)(j * BC) * p.ks_t, p.ks_t, nkeys, tid);
-    stage_tile<D, BC>(sm.v, vbase + (int64_t)(j * BC) * p.vs_t, p.vs_t, nkeys, tid);
-    __syncthreads();
+    if (e + 1 < e1) fetch(e + 1);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
       f32x16 s = f32x16{}, dp = f32x16{};
