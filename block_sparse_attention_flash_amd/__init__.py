@@ -331,7 +331,7 @@ def prefill_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
 
 def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
                      row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
-                     dq=None, dk=None, dv=None, workspace=None) -> Plan:
+                     dq=None, dk=None, dv=None, workspace=None, block_state=None) -> Plan:
     """Marshal a backward (arguments as ``prefill_bwd``) into a reusable Plan
     whose call returns (dq, dk, dv)."""
     torch = _torch()
@@ -361,23 +361,26 @@ def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, 
     a.Br, a.Bc = 128, 64
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
-    keep = (q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx, workspace)
+    a.block_state = _ptr(block_state)
+    keep = (q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx, workspace, block_state)
     return Plan(library().bsattn_prefill_bwd, a, (dq, dk, dv), keep)
 
 
 def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
                 row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
-                dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Gradients of the static block-sparse forward (lambda = 0) for the loss
+                dq=None, dk=None, dv=None, workspace=None, block_state=None, stream=None):
+    """Gradients of the block-sparse forward for the loss
     sum(out * dout): q, out, dout [B, Nq, Hq, d], k, v [B, Nk, Hkv, d] bf16,
     ``lse`` float32 [B, Hq, Nq] from ``prefill_fwd(..., lse=)``.  The mask
     arguments are the forward's; with a CSR, ``col_ptr``/``row_idx`` are the
     device copies of ``transpose_block_index``.  ``workspace`` (uint8, at
     least ``prefill_bwd_workspace_size`` bytes) is allocated here if None.
-    Returns (dq, dk, dv)."""
+    After a forward with lambda > 0, pass its ``block_state`` (uint8
+    [B, Hq, Tr, Tc]): the blocks it skipped get no gradient.  Returns
+    (dq, dk, dv)."""
     return prefill_bwd_plan(q, k, v, out, dout, lse, scale=scale, causal=causal, row_ptr=row_ptr,
                             col_idx=col_idx, col_ptr=col_ptr, row_idx=row_idx, n_valid=n_valid, dq=dq, dk=dk,
-                            dv=dv, workspace=workspace)(stream)
+                            dv=dv, workspace=workspace, block_state=block_state)(stream)
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:

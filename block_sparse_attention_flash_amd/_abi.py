@@ -69,7 +69,8 @@ class BwdArgs(C.Structure):
                 ("dk_stride", C.c_int64 * 3), ("dv_stride", C.c_int64 * 3),
                 ("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("col_ptr", C.c_void_p), ("row_idx", C.c_void_p),
                 ("n_valid", C.c_int32), ("scale", C.c_float), ("causal", C.c_int32), ("Br", C.c_int32),
-                ("Bc", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("Bc", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("block_state", C.c_void_p)]
 
 
 class DecodeArgs(C.Structure):

@@ -261,6 +261,7 @@ bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream)
   p.causal = a->causal ? 1 : 0;
   p.Tr = (a->Nq + 127) / 128;
   p.Tc = (a->Nk + 63) / 64;
+  p.block_state = a->block_state;
   if ((int64_t)p.B * p.Hq * p.Tr > 0x7fffffffLL || (int64_t)p.B * p.Hkv * p.Tc > 0x7fffffffLL ||
       (int64_t)p.B * p.Hq * p.Nq > 0x7fffffffLL)
     return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");

@@ -81,6 +81,7 @@ struct BwdParams {
   float scale;
   int32_t causal;
   int32_t Tr, Tc;
+  const uint8_t* block_state;   // optional [B][Hq][Tr][Tc] of a skipping forward: 2 = no gradient
 };
 
 int launch_prefill_bwd(const BwdParams& p, void* stream);

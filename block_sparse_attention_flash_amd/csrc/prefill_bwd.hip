@@ -241,6 +241,7 @@ __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const
     const int t = __builtin_amdgcn_readfirstlane(p.row_idx ? p.row_idx[e] : e);
     const int row0 = t * BR + 64 * hf;
     if (row0 >= p.Nq || (CAUSAL && row0 + 63 < j * BC)) continue;
+    if (p.block_state && p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] == 2) continue;
     const int nrows = min(64, p.Nq - row0);
     __syncthreads();  // every wave is done reading the previous stage
     dma_tile64<D>(sm.q, static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h, p.Nq, p.qs_t,
@@ -399,6 +400,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
     nv.load(vbase + (int64_t)(j * BC) * p.vs_t, p.vs_t, nkeys, tid);
   };
   if (e0 < e1) fetch(e0);
+  const uint8_t* skipped = p.block_state ? p.block_state + (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc : nullptr;
   for (int e = e0; e < e1; ++e) {
     const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
     __syncthreads();  // every wave is done reading the previous block
@@ -406,6 +408,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
     nv.store(sm.v, tid);
     __syncthreads();
     if (e + 1 < e1) fetch(e + 1);
+    if (skipped && skipped[j] == 2) continue;  // the forward skipped it: no gradient (uniform branch)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
       f32x16 s = f32x16{}, dp = f32x16{};

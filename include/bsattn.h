@@ -230,8 +230,9 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
 /* ------------------------------------------------------------------------ */
 
 /*
- * Gradients of the static block-sparse attention computed by
- * bsattn_prefill_fwd with lambda = 0: for the loss sum(out * dout),
+ * Gradients of the block-sparse attention computed by bsattn_prefill_fwd
+ * (lambda = 0, or lambda > 0 with that call's block_state passed in, which
+ * drops the blocks it skipped): for the loss sum(out * dout),
  *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
  *   P = the forward's softmax over each row's attended keys (rebuilt from
  *       q, k and the forward's lse), dP = dout V^T,
@@ -281,6 +282,11 @@ typedef struct {
   void* workspace;        /* device, >= bsattn_prefill_bwd_workspace_size(B, Hq, Nq) bytes,
                              256-byte aligned; no initial contents needed */
   size_t workspace_bytes;
+  const uint8_t* block_state; /* optional device [B, Hq, Tr, Tc]: the block_state a forward with
+                             lambda > 0 wrote; blocks it skipped (2) get no gradient, so the
+                             gradients are those of the function that forward computed (softmax
+                             over its kept blocks; BLASST notes, training with the skipping
+                             forward).  NULL = every visited block */
 } bsattn_prefill_bwd_args;
 
 /* Workspace bytes of a backward call (one float per query row and head). */

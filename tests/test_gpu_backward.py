@@ -173,3 +173,57 @@ def test_backward_cfg2_full_size_sampled():
         compare_grad(sl(dv), rv, f"dv b{b} h{h}")
         rl = BW.prefill_lse(sl(q), sl(k), mask, cfg.scale)[0, 0]
         assert np.abs(lse[b, h] - rl).max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_after_skipping_forward(d):
+    """BLASST forward (lambda > 0, causal GQA, the sink recipe so that blocks
+    are skipped), then the backward with that forward's block_state: the
+    gradients are those of softmax attention over each tile's kept blocks.
+    The oracle takes its own skip decisions (Algorithm 1); where a decision
+    lies within the accepted margin of the threshold it follows the GPU's,
+    as the forward tests do."""
+    from oracle import attention as A
+    from _parity import MARGIN
+    N, lam = 1000, 0.3
+    cfg = PrefillWorkload(name="bwd_skip", description="", dtype="bf16", B=1, Hq=8, Hkv=2, N=N, d=d, Br=128,
+                          Bc=64, causal=True, lam=lam, mask=None, seed=231, generator="sink")
+    _say(f"backward after a skipping forward: causal GQA 8/2 N{N} d{d} lambda {lam}")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, dout))
+    Tr, Tc = -(-N // 128), -(-N // 64)
+    state = torch.zeros((1, 8, Tr, Tc), dtype=torch.uint8, device=DEV)
+    lse = torch.empty((1, 8, N), dtype=torch.float32, device=DEV)
+    out = bsa.prefill_fwd(qd, kd, vd, scale=cfg.scale, lam=lam, causal=True, block_state=state, lse=lse)
+    dq, dk, dv = bsa.prefill_bwd(qd, kd, vd, out, gd, lse, scale=cfg.scale, causal=True, block_state=state)
+    torch.cuda.synchronize()
+    st = state.cpu().numpy()
+    dq, dk, dv, lse = dq.cpu(), dk.cpu(), dv.cpu(), lse.cpu().numpy()
+    rq = np.zeros((1, N, 8, d))
+    rk = np.zeros((1, N, 2, d))
+    rv = np.zeros((1, N, 2, d))
+    n_skip = 0
+    for h in range(8):
+        tm = np.zeros((Tr, Tc), bool)
+        for t in range(Tr):
+            rows, _, blocks, skip, margin = A.prefill_tile(q, k, v, 0, h, t, Br=128, Bc=64, scale=cfg.scale,
+                                                          causal=True, lam=lam, n_valid=N)
+            g_skip = st[0, h, t, blocks] == 2
+            bad = (g_skip != skip) & ~(np.abs(margin) <= MARGIN)
+            assert not bad.any(), f"skip set differs at h{h} t{t}"
+            tm[t, blocks[~g_skip]] = True          # oracle decisions, GPU's only inside the margin
+            n_skip += int(g_skip.sum())
+        mask = M.expand_token_mask(tm, N, N, 128, 64, N, True)
+        g = h // 4
+        hq, hk, hv = BW.masked_attention_grads(q[0, :, h], k[0, :, g], v[0, :, g], dout[0, :, h], mask, cfg.scale)
+        rq[0, :, h] = hq
+        rk[0, :, g] += hk
+        rv[0, :, g] += hv
+        rl = BW.row_lse(q[0, :, h], k[0, :, g], mask, cfg.scale)
+        assert np.abs(lse[0, h] - rl).max() <= LSE_ABS
+    _say(f"  blocks skipped by the forward: {n_skip}")
+    assert n_skip > 0
+    compare_grad(dq, rq, "dq")
+    compare_grad(dk, rk, "dk")
+    compare_grad(dv, rv, "dv")
