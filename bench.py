@@ -343,7 +343,7 @@ def sweep_prefill(name: str, lams, steps: int, warmup: int):
     res = []
     base_ms = None
     for lam in lams:
-        use_sched = sched if lam == 0.0 else None  # cut tiles are exact only for lambda = 0
+        use_sched = sched  # with lambda > 0 a chunk-maximum pass keeps cut tiles exact
         cnt = torch.zeros((cfg.B, cfg.Hq, Tr, 2), dtype=torch.int32, device=dev)
         rowc = torch.zeros((cfg.B, cfg.Hq, Tr), dtype=torch.int32, device=dev)
 

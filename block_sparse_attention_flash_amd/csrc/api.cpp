@@ -74,6 +74,7 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   w.ml = off;  off = align256(off + units * 128 * 2 * sizeof(float));
   w.cnt = off; off = align256(off + units * 2 * sizeof(int32_t));
   w.arrive = off; off = align256(off + units * sizeof(int32_t));  // n_merges <= n_slots
+  w.pre = off; off = align256(off + units * 128 * sizeof(float));
   w.total = off;
   return w;
 }
@@ -183,8 +184,6 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
     if (a->n_slots < 0 || a->n_merges < 0 || (a->n_merges > 0) != (a->n_slots > 0) || (a->n_merges > 0 && !a->sched_merges) ||
         a->n_merges > a->n_slots)
       return fail(BSATTN_ERR_INVALID_ARG, "inconsistent schedule counts (n_merges, n_slots, sched_merges)");
-    if (a->n_slots > 0 && a->lambda > 0.0f)
-      return fail(BSATTN_ERR_UNSUPPORTED, "a schedule that cuts tiles needs lambda == 0 (BLASST decisions span the row)");
     if (a->n_slots > 0) {
       const PrefillWorkspace w = prefill_workspace_layout(a->B, a->Hq, a->d, a->n_slots);
       if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
@@ -196,6 +195,7 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
       p.part_ml = reinterpret_cast<float*>(ws + w.ml);
       p.part_cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
       p.arrive = reinterpret_cast<int32_t*>(ws + w.arrive);
+      p.part_pre = reinterpret_cast<float*>(ws + w.pre);
     }
     p.sched_items = a->sched_items; p.n_items = a->n_items;
     p.sched_merges = a->sched_merges; p.n_merges = a->n_merges; p.n_slots = a->n_slots;

@@ -49,6 +49,7 @@ struct PrefillParams {
   float* part_ml;               // [n_slots][B][Hq][128][2]  (reference max in raw score units, row sum)
   int32_t* part_cnt;            // [n_slots][B][Hq][2]
   int32_t* arrive;              // [n_merges][B][Hq] chunk arrival counters (zero between calls)
+  float* part_pre;              // [n_slots][B][Hq][128] lambda > 0: per-row max of each chunk
   int32_t rank_major;           // bf16 kernel: XCD work order (set by its launcher)
   float* lse;                   // optional [B][Hq][Nq] natural-log row sums of exp
 };
@@ -87,7 +88,7 @@ struct BwdParams {
 int launch_prefill_bwd(const BwdParams& p, void* stream);
 
 struct PrefillWorkspace {
-  size_t o, ml, cnt, arrive, total;
+  size_t o, ml, cnt, arrive, pre, total;
 };
 PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int32_t n_slots);
 

@@ -185,7 +185,13 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 template <int D>
 constexpr int kMinBlocksPerCu = D == 64 ? 3 : 2;
 
-template <int D, bool CAUSAL, bool DYN>
+// MAXONLY (with DYN): the pass that runs before a skipping launch whose
+// schedule cuts tiles.  Each chunk of a cut tile writes, per query row, the
+// maximum score over its blocks (no exponentials, no V); the main pass then
+// starts a chunk's running max at the maximum of the chunks visited before
+// it, which is the running max Algorithm 1 reaches there, so cut tiles take
+// exactly the skip decisions of a whole-row walk.
+template <int D, bool CAUSAL, bool DYN, bool MAXONLY>
 __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(const PrefillParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the launch stub
   constexpr int KS = D / 16;  // k-steps of the S MFMA
@@ -252,6 +258,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   e1 = __builtin_amdgcn_readfirstlane(e1);
   slot = __builtin_amdgcn_readfirstlane(slot);
   mrg = __builtin_amdgcn_readfirstlane(mrg);
+  if (MAXONLY && slot < 0) return;  // only chunks of cut tiles need their maxima
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
@@ -292,6 +299,16 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const float c2 = p.scale * kLog2e;                    // raw score -> log2 units
   const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
   float m_run = kNegInf;   // true running max (raw score units)
+  if (DYN && !MAXONLY && slot >= 0) {
+    // a chunk of a cut tile starts from the maxima of the chunks visited
+    // before it (ascending: lower slots; descending: higher slots)
+    const int s0 = p.sched_merges[3 * mrg + 1];
+    const int ns = p.sched_merges[3 * mrg + 2];
+    const int lo = p.block_order ? slot + 1 : s0, hi_s = p.block_order ? s0 + ns : slot;
+    for (int sl = lo; sl < hi_s; ++sl)
+      m_run = fmaxf(m_run, p.part_pre[(((int64_t)sl * p.B + b) * p.Hq + h) * BR + wave * 32 + l32]);
+  }
+  float m_chunk = kNegInf;  // MAXONLY: this row's maximum over the chunk
   float m_ref = kNegInf;   // reference max used in the exponent (raw units)
   // Row sums.  At d = 64 the vector ALUs are the busier unit, so the sums run
   // on the matrix core: an all-ones A operand makes every element of lacc in
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   auto fetch = [&](int i, int jj) __attribute__((always_inline)) {
     const int stg = i % ST;
     ksrc.issue(sm.k[stg], p.ks_t, jj, wave);
-    vsrc.issue(sm.v[stg], p.vs_t, jj, wave);
+    if constexpr (!MAXONLY) vsrc.issue(sm.v[stg], p.vs_t, jj, wave);
   };
   // block indices of blocks it .. it+3; the farthest is read a full iteration
   // (two at two stages) before its loads are issued
@@ -401,6 +418,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       mb1 = fmaxf(mb1, sacc[1][a]);
     }
     const float mb = wave_max_xor32(fmaxf(mb0, mb1));
+    if constexpr (MAXONLY) {
+      m_chunk = fmaxf(m_chunk, mb);
+      if constexpr (ST == 3) q3 = blk(it + 4);
+      else q2 = blk(it + 3);
+      continue;
+    }
     const float m_new = fmaxf(m_run, mb);
 
     bool skip = false;
@@ -480,6 +503,10 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     // block's LDS traffic (its wait then costs nothing where it is used)
     if constexpr (ST == 3) q3 = blk(it + 4);
     else q2 = blk(it + 3);
+  }
+  if constexpr (MAXONLY) {
+    if (hi == 0) p.part_pre[(((int64_t)slot * p.B + b) * p.Hq + h) * BR + wave * 32 + l32] = m_chunk;
+    return;
   }
   float l_tot;
   if constexpr (kSumOnMfma) {
@@ -612,7 +639,12 @@ hipError_t launch(const PrefillParams& p0, hipStream_t s) {
   const int64_t grid = (int64_t)p.B * p.Hq * units;
   // rank-major when one XCD (32 CUs) has under four waves of work-groups
   p.rank_major = grid / 8 < 4 * 32 * kMinBlocksPerCu<D> ? 1 : 0;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, DYN>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+  if (DYN && p.n_slots > 0) {  // cut tiles: the chunk maxima first (same grid, uncut items return)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, true>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, DYN, false>), dim3((unsigned)grid), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

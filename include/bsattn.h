@@ -142,9 +142,11 @@ bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t*
  * (running max, row sum, unnormalised output) to the prefill workspace; the
  * last chunk of a cut tile to finish combines the partials with the online-
  * softmax rescaling rule (attention tutorial section 4.2), in slot order, and
- * writes the output.  Exact for lambda = 0; a schedule that cuts tiles is
- * refused for lambda > 0, whose skip decisions depend on the whole row
- * (BLASST notes Algorithm 1).
+ * writes the output.  With lambda > 0 the skip decisions depend on the
+ * running max of every block visited before (BLASST notes Algorithm 1): a
+ * first pass over the chunks of cut tiles writes each chunk's per-row block
+ * maximum, and every chunk then starts from the maximum of the chunks
+ * visited before it, so the decisions equal those of a whole-row walk.
  *   items  [n_items][5]  {tile, first CSR entry, end CSR entry, slot, merge};
  *                        slot = merge = -1 means the item writes the output
  *                        directly, else merge indexes `merges`; items are
@@ -200,7 +202,7 @@ typedef struct {
   int32_t n_items;
   const int32_t* sched_merges; /* device copy of the schedule's merges (NULL if n_merges == 0) */
   int32_t n_merges;
-  int32_t n_slots;             /* partial slots of the schedule; > 0 requires lambda == 0 */
+  int32_t n_slots;             /* partial slots of the schedule (cut tiles) */
   void* workspace;             /* device, >= bsattn_prefill_workspace_size(B, Hq, d, n_slots) bytes,
                                   256-byte aligned; unused when n_slots == 0.  Holds the
                                   partials and one arrival counter per (merge, batch, head):

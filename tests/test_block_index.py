@@ -165,10 +165,11 @@ def test_schedule_validation():
     assert st == _abi.BSATTN_ERR_INVALID_ARG                         # schedule without CSR
     a.row_ptr = a.col_idx = 0x30000
     a.sched_merges, a.n_merges, a.n_slots = 0x40000, 1, 2
-    a.lam = 0.1
-    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_UNSUPPORTED   # cut tiles + BLASST
-    a.lam = 0.0
+    a.lam = 0.1                                                    # cut tiles + BLASST: accepted,
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG   # needs its workspace
     a.workspace, a.workspace_bytes = 0x50000, 16
+    assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_CAPACITY
+    a.lam = 0.0
     assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_CAPACITY
     a.n_merges = 0
     assert lib.bsattn_prefill_fwd(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG   # inconsistent counts

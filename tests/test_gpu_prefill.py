@@ -251,6 +251,38 @@ def test_schedule_cut_tiles_small(max_blocks):
                                        causal=False, lam=0.0, n_valid=spec.n_valid, row_ptr=csr[0], col_idx=csr[1])
 
 
+@pytest.mark.parametrize("max_blocks,order,causal", [(3, "ascending", False), (2, "descending", False),
+                                                    (3, "ascending", True), (1, "descending", True)])
+def test_schedule_cut_tiles_dynamic(max_blocks, order, causal):
+    """lambda > 0 with tiles cut into chunks: the chunk-maximum pass lets each
+    chunk start from the running max of the chunks visited before it, so skip
+    sets, counters and outputs match the whole-row oracle walk."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid
+    lam = 0.3
+    gen = "sink" if order == "ascending" else "sink_last"  # the dominant block is visited first
+    tot = [0, 0, 0]
+    for d in (64, 128):
+        cfg = _small("sched_dyn", N=n, d=d, Hq=4, Hkv=2, mask=spec, generator=gen, causal=causal, lam=lam)
+        _say(f"schedule max_blocks {max_blocks} lambda {lam} {order} causal {causal} d{d}")
+        q, k, v = gen_prefill_inputs(cfg)
+        csr = bsa.build_block_index(spec, n, n, 128, 64)
+        sched = bsa.build_schedule(csr[0], max_blocks)
+        assert sched.n_slots > 0
+        ws = bsa.prefill_workspace(cfg.B, cfg.Hq, d, sched.n_slots, DEV)
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched, workspace=ws,
+                                   block_order=order)
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                for t in range(-(-n // 128)):
+                    r = check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale,
+                                           causal=causal, lam=lam, n_valid=n, row_ptr=csr[0], col_idx=csr[1],
+                                           order=order)
+                    tot = [x + y for x, y in zip(tot, r)]
+    _say(f"  visited {tot[0]} skipped {tot[1]} excused {tot[2]}")
+    assert tot[1] > 0
+
+
 def test_cfg3_full_size_schedule():
     cfg = get_config("cfg3")
     _say("cfg3 with the default schedule (anchor tile cut into chunks)")

@@ -76,7 +76,7 @@ class PrefillWorkload:
     lam: float                 # 0 = no dynamic skipping
     mask: Optional[MaskSpec]   # None = dense (or dense causal)
     seed: int
-    generator: str             # "iid", "iid_offset", "concentrated"
+    generator: str             # "iid", "iid_offset", "concentrated", "sink", "sink_last"
 
     @property
     def scale(self) -> float:

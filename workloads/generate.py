@@ -26,6 +26,8 @@ Generator readings (the workload text names them, the pages do not):
   every Q, K and V row of that head.
 * "sink" (test recipe for the skip path): every query gets 4 w and the first
   64 keys get 10 w, w one random unit direction shared by all heads.
+* "sink_last": the same with the sink on the last 64 keys (test recipe for
+  the recent-first order).
 """
 
 from __future__ import annotations
@@ -93,7 +95,7 @@ def gen_prefill_inputs(cfg: PrefillWorkload, device="cpu", B=None, N=None):
         mq = q.view(B, N, Hkv, G, d).mean(dim=(1, 3))          # [B, Hkv, d]
         ns = min(64, N)
         k[:, :ns] += 4.0 * mq[:, None, :, :]
-    elif cfg.generator == "sink":
+    elif cfg.generator in ("sink", "sink_last"):
         # a shared query direction w (norm 4) and a sink of 64 keys along w
         # (norm 10): scores against the sink exceed the others by ~40*scale,
         # so whole key blocks fall below the BLASST threshold
@@ -101,7 +103,10 @@ def gen_prefill_inputs(cfg: PrefillWorkload, device="cpu", B=None, N=None):
         w = w / w.norm()
         q += 4.0 * w
         ns = min(64, N)
-        k[:, :ns] += 10.0 * w
+        if cfg.generator == "sink":
+            k[:, :ns] += 10.0 * w
+        else:  # the mirror: the sink is the last 64 keys (found first when recent blocks go first)
+            k[:, N - ns:] += 10.0 * w
     elif cfg.generator != "iid":
         raise ValueError(cfg.generator)
     dt = _store_dtype(cfg)
