@@ -10,6 +10,8 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 
 * ``build_block_index(spec, n_q, n_k, Br, Bc)`` -> (row_ptr, col_idx) int32 numpy
 * ``validate_block_index(row_ptr, col_idx, Tc)``
+* ``block_index_from_matrix(m)``, ``block_index_from_bitmap(bits, Tr, Tc)``,
+  ``block_index_from_coo(rows, cols, Tr, Tc)`` -> (row_ptr, col_idx)
 * ``tile_order_lpt(row_ptr)`` -> int32 numpy launch order
 * ``build_schedule(row_ptr, max_blocks_per_item)`` -> Schedule (host arrays, counts)
 * ``prefill_workspace_size(B, Hq, d, n_slots)``, ``prefill_workspace(...)`` (zero-filled)
@@ -38,6 +40,7 @@ from . import _abi
 
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
+    "block_index_from_matrix", "block_index_from_bitmap", "block_index_from_coo",
     "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace",
     "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_plan", "prefill_bwd_workspace_size", "transpose_block_index",
     "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits",
@@ -126,6 +129,40 @@ def validate_block_index(row_ptr, col_idx, Tc: int):
     col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
     _check(library().bsattn_validate_block_index(row_ptr.ctypes.data, col_idx.ctypes.data if col_idx.size else None,
                                                  row_ptr.size - 1, Tc))
+
+
+def _csr_two_call(fn, head_args, Tr: int):
+    row_ptr = np.zeros(Tr + 1, np.int32)
+    nnz = C.c_int64(0)
+    _check(fn(*head_args, row_ptr.ctypes.data, None, 0, C.byref(nnz)))
+    col_idx = np.zeros(max(1, nnz.value), np.int32)
+    _check(fn(*head_args, row_ptr.ctypes.data, col_idx.ctypes.data, col_idx.size, C.byref(nnz)))
+    return row_ptr, col_idx[:nnz.value].copy()
+
+
+def block_index_from_matrix(m):
+    """CSR of a 0/1 block matrix (host array [Tr, Tc], nonzero = kept)."""
+    m = np.ascontiguousarray(m, dtype=np.uint8)
+    Tr, Tc = m.shape
+    return _csr_two_call(library().bsattn_block_index_from_matrix, (m.ctypes.data, Tr, Tc), Tr)
+
+
+def block_index_from_bitmap(bits, Tr: int, Tc: int):
+    """CSR of a block bitmap: bit t * Tc + j (LSB first) set = kept."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    if bits.size * 8 < Tr * Tc:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "bitmap shorter than Tr * Tc bits")
+    return _csr_two_call(library().bsattn_block_index_from_bitmap, (bits.ctypes.data, Tr, Tc), Tr)
+
+
+def block_index_from_coo(rows, cols, Tr: int, Tc: int):
+    """CSR of COO (row, col) pairs of kept blocks (any order, duplicates allowed)."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    if rows.shape != cols.shape:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "rows and cols differ in length")
+    return _csr_two_call(library().bsattn_block_index_from_coo,
+                         (rows.ctypes.data, cols.ctypes.data, rows.size, Tr, Tc), Tr)
 
 
 def transpose_block_index(row_ptr, col_idx, Tc: int):

@@ -23,6 +23,7 @@ EXPORTED = (
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
     "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
     "bsattn_transpose_block_index", "bsattn_prefill_bwd_workspace_size", "bsattn_prefill_bwd",
+    "bsattn_block_index_from_matrix", "bsattn_block_index_from_bitmap", "bsattn_block_index_from_coo",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
     "bsattn_decode_fwd", "bsattn_decode_check",
     "bsattn_calibrate_threshold",
@@ -112,6 +113,13 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_prefill_workspace_size.argtypes = [C.c_int32] * 4
     lib.bsattn_prefill_fwd.restype = C.c_int
     lib.bsattn_prefill_fwd.argtypes = [C.POINTER(PrefillArgs), C.c_void_p]
+    for fn in ("bsattn_block_index_from_matrix", "bsattn_block_index_from_bitmap"):
+        getattr(lib, fn).restype = C.c_int
+        getattr(lib, fn).argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int64,
+                                     C.POINTER(C.c_int64)]
+    lib.bsattn_block_index_from_coo.restype = C.c_int
+    lib.bsattn_block_index_from_coo.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+                                                C.c_void_p, C.c_int64, C.POINTER(C.c_int64)]
     lib.bsattn_transpose_block_index.restype = C.c_int
     lib.bsattn_transpose_block_index.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
                                                  C.c_void_p]

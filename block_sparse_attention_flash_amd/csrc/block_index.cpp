@@ -200,6 +200,34 @@ bsattn_status build_block_index(const bsattn_mask_spec* spec, int32_t n_q, int32
 
 }  // namespace bsattn
 
+namespace {
+
+// CSR of a kept-block predicate, tile-major and ascending within a tile.
+template <class Kept>
+bsattn_status csr_of(Kept kept, int32_t Tr, int32_t Tc, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                     int64_t* nnz_out) {
+  using namespace bsattn;
+  if (!row_ptr || !nnz_out || Tr < 1 || Tc < 1) return fail(BSATTN_ERR_INVALID_ARG, "row_ptr / nnz_out NULL or Tr, Tc < 1");
+  int64_t nnz = 0;
+  row_ptr[0] = 0;
+  for (int32_t t = 0; t < Tr; ++t) {
+    for (int32_t j = 0; j < Tc; ++j) {
+      if (!kept(t, j)) continue;
+      if (col_idx) {
+        if (nnz >= col_capacity) return fail(BSATTN_ERR_CAPACITY, "col_idx capacity %lld too small", (long long)col_capacity);
+        col_idx[nnz] = j;
+      }
+      ++nnz;
+    }
+    if (nnz > 0x7fffffffLL) return fail(BSATTN_ERR_CAPACITY, "more than 2^31 - 1 kept blocks");
+    row_ptr[t + 1] = (int32_t)nnz;
+  }
+  *nnz_out = nnz;
+  return BSATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 bsattn_status bsattn_build_block_index(const bsattn_mask_spec* spec, int32_t n_q, int32_t n_k, int32_t Br,
@@ -244,6 +272,46 @@ bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t*
     }
   }
   return BSATTN_OK;
+}
+
+bsattn_status bsattn_block_index_from_matrix(const uint8_t* m, int32_t Tr, int32_t Tc, int32_t* row_ptr,
+                                             int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out) {
+  using namespace bsattn;
+  clear_error();
+  if (!m) return fail(BSATTN_ERR_INVALID_ARG, "block matrix is NULL");
+  return csr_of([&](int32_t t, int32_t j) { return m[(int64_t)t * Tc + j] != 0; }, Tr, Tc, row_ptr, col_idx,
+                col_capacity, nnz_out);
+}
+
+bsattn_status bsattn_block_index_from_bitmap(const uint8_t* bits, int32_t Tr, int32_t Tc, int32_t* row_ptr,
+                                             int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out) {
+  using namespace bsattn;
+  clear_error();
+  if (!bits) return fail(BSATTN_ERR_INVALID_ARG, "bitmap is NULL");
+  return csr_of(
+      [&](int32_t t, int32_t j) {
+        const int64_t k = (int64_t)t * Tc + j;
+        return ((bits[k >> 3] >> (k & 7)) & 1) != 0;
+      },
+      Tr, Tc, row_ptr, col_idx, col_capacity, nnz_out);
+}
+
+bsattn_status bsattn_block_index_from_coo(const int32_t* rows, const int32_t* cols, int64_t n, int32_t Tr,
+                                          int32_t Tc, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                          int64_t* nnz_out) {
+  using namespace bsattn;
+  clear_error();
+  if (n < 0 || (n > 0 && (!rows || !cols))) return fail(BSATTN_ERR_INVALID_ARG, "rows / cols NULL or n < 0");
+  if (Tr < 1 || Tc < 1) return fail(BSATTN_ERR_INVALID_ARG, "Tr, Tc must be >= 1");
+  std::vector<uint8_t> m((size_t)Tr * Tc, 0);
+  for (int64_t x = 0; x < n; ++x) {
+    if (rows[x] < 0 || rows[x] >= Tr || cols[x] < 0 || cols[x] >= Tc)
+      return fail(BSATTN_ERR_INVALID_ARG, "pair %lld = (%d, %d) outside [0, %d) x [0, %d)", (long long)x, rows[x],
+                  cols[x], Tr, Tc);
+    m[(size_t)rows[x] * Tc + cols[x]] = 1;
+  }
+  return csr_of([&](int32_t t, int32_t j) { return m[(size_t)t * Tc + j] != 0; }, Tr, Tc, row_ptr, col_idx,
+                col_capacity, nnz_out);
 }
 
 bsattn_status bsattn_transpose_block_index(const int32_t* row_ptr, const int32_t* col_idx, int32_t Tr, int32_t Tc,

@@ -117,6 +117,25 @@ bsattn_status bsattn_build_block_index(const bsattn_mask_spec* spec, int32_t n_q
                                        int32_t Br, int32_t Bc, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int64_t* nnz_out);
 
+/* The same CSR from the block-mask forms the DiT article's mask flow produces
+ * (section 2.3: a 0/1 matrix over (query block, key block), stored as a
+ * bitmap of one bit per block or as COO pairs; section 3.2):
+ *   _from_matrix  uint8 [Tr][Tc] row-major, nonzero = kept
+ *   _from_bitmap  bit (t * Tc + j) of the byte string, least significant bit
+ *                 first, set = kept ((Tr * Tc + 7) / 8 bytes)
+ *   _from_coo     n (row, col) pairs of kept blocks, any order, duplicates
+ *                 allowed; a pair outside [0, Tr) x [0, Tc) is INVALID_ARG
+ * Host buffers, two-call pattern as bsattn_build_block_index (col_idx NULL
+ * returns the count in *nnz_out; BSATTN_ERR_CAPACITY if col_capacity is
+ * short).  Tiles list their blocks in ascending order. */
+bsattn_status bsattn_block_index_from_matrix(const uint8_t* m, int32_t Tr, int32_t Tc, int32_t* row_ptr,
+                                             int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out);
+bsattn_status bsattn_block_index_from_bitmap(const uint8_t* bits, int32_t Tr, int32_t Tc, int32_t* row_ptr,
+                                             int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out);
+bsattn_status bsattn_block_index_from_coo(const int32_t* rows, const int32_t* cols, int64_t n, int32_t Tr,
+                                          int32_t Tc, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                          int64_t* nnz_out);
+
 /* Check a host CSR: row_ptr[0] == 0, nondecreasing, row_ptr[Tr] = nnz,
  * col_idx strictly ascending within each tile and inside [0, Tc). */
 bsattn_status bsattn_validate_block_index(const int32_t* row_ptr, const int32_t* col_idx,

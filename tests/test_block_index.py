@@ -195,3 +195,32 @@ def test_transpose_block_index():
         bsa.transpose_block_index(np.array([0, 2], np.int32), np.array([1, 0], np.int32), 4)   # not ascending
     with pytest.raises(bsa.BsattnError):
         bsa.transpose_block_index(np.array([0, 1], np.int32), np.array([4], np.int32), 4)      # out of range
+
+
+def test_block_index_from_matrix_bitmap_coo():
+    """The block-mask forms of the DiT article (0/1 matrix, one-bit-per-block
+    bitmap, COO pairs) give the oracle's CSR of the same matrix; the bitmap
+    has the article's size; bad input is refused."""
+    g = np.random.default_rng(9)
+    for Tr, Tc in ((1, 1), (3, 5), (34, 68), (9, 2)):
+        tm = g.random((Tr, Tc)) < 0.3
+        tm[0] = False
+        ref = M.csr_from_tile_mask(tm)
+        got = bsa.block_index_from_matrix(tm)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+        bits = np.packbits(tm.reshape(-1), bitorder="little")
+        assert bits.size == M.bitmap_bytes(Tr, Tc)
+        got = bsa.block_index_from_bitmap(bits, Tr, Tc)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+        r, c = np.nonzero(tm)
+        perm = g.permutation(r.size)
+        r2, c2 = np.concatenate([r[perm], r[:3]]), np.concatenate([c[perm], c[:3]])   # shuffled, duplicates
+        got = bsa.block_index_from_coo(r2, c2, Tr, Tc)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+        bsa.validate_block_index(got[0], got[1], Tc)
+    with pytest.raises(bsa.BsattnError):
+        bsa.block_index_from_coo(np.array([0, 3]), np.array([0, 0]), 3, 4)      # row out of range
+    with pytest.raises(bsa.BsattnError):
+        bsa.block_index_from_coo(np.array([0]), np.array([-1]), 3, 4)            # col out of range
+    with pytest.raises(bsa.BsattnError):
+        bsa.block_index_from_bitmap(np.zeros(1, np.uint8), 3, 4)                # 8 bits < 12 blocks
