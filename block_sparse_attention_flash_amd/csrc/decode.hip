@@ -19,12 +19,14 @@
 //            splits for their inclusive prefix, publish the inclusive prefix
 //   phase 2  running max within the split seeded with the exclusive prefix,
 //            tile-wide skip decision per block (strict <, as printed)
-//   phase 3  kept blocks only: reload K (the scores are recomputed, bit for
-//            bit the phase-1 values: same MFMA on the same data) and load V,
+//   phase 3  kept blocks only: their scores (kept in LDS since phase 1 where
+//            that costs no occupancy, else recomputed bit for bit from a K
+//            reload: same MFMA on the same data) and V,
 //            P = 2^(s - m_ref), O_partial = P V on the vector ALUs (G <= 8
-//            rows), write the partial (m_ref, l, O) of the split.  Keeping the
-//            scores out of LDS keeps the work-group small, so enough of them
-//            share a CU to keep HBM busy while some sit in phases 2-3.
+//            rows), write the partial (m_ref, l, O) of the split.  Where the
+//            registers do not already hold a CU to two work-groups, the
+//            scores stay out of LDS: the work-group stays small, so enough of
+//            them share a CU to keep HBM busy while some sit in phases 2-3.
 //   combine  merge the splits of each (sequence, head): online-softmax
 //            rescaling (attention tutorial section 4.2); it also clears the
 //            pair's ticket and look-back flags, so the workspace needs no
@@ -70,8 +72,15 @@ __device__ __forceinline__ int spin_flag(const int* flag, int* health) {
   return 0;
 }
 
+// Phase 1 keeps every block's scores in LDS for phase 3 (no K reload for kept
+// blocks) where that costs no occupancy: at d = 128 with G <= 4 the registers
+// already limit a CU to two work-groups, and 64 KB more LDS still fits two.
+template <int D, int G>
+constexpr bool kKeepScores = D == 128 && G <= 4;
+
 template <int D, int G>
 struct DecSmem {
+  float sc[kKeepScores<D, G> ? 64 : 1][64][4];  // scores [block][key][row] (rows 0..3)
   float bm[64][G];              // block row maxima (log2 units)
   float m_ref[G];
   float lsum[4][G];
@@ -169,6 +178,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       if (lb + 4 < nb) load_k_block<D>(knxt, kbase, p.ks_t, blk0 + lb + 4, p.L, r16, q16);
       f32x4 acc[4];
       block_scores<D>(acc, kcur, qa, c2, blk0 + lb, p.L, r16);
+      if constexpr (kKeepScores<D, G>) {
+        if (q16 == 0)  // rows 0..3: lanes 0..15 hold key 16 kt + lane
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f32x4*>(&sm.sc[lb][16 * kt + r16][0]) = acc[kt];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = fmaxf(fmaxf(acc[0][i], acc[1][i]), fmaxf(acc[2][i], acc[3][i]));
@@ -304,7 +318,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) mb[i] = ((rskip_l[i] >> lb) & 1ull) ? kPosInf : mref_l[i];
     bf16x8 kf[4][KS];
-    load_k_block<D>(kf, kbase, p.ks_t, j, p.L, r16, q16);
+    if constexpr (!kKeepScores<D, G>) load_k_block<D>(kf, kbase, p.ks_t, j, p.L, r16, q16);
     u32x4 vv[STEPS];
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
@@ -313,7 +327,12 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
                          : u32x4{0, 0, 0, 0};
     }
     f32x4 sc[4];
-    block_scores<D>(sc, kf, qa, c2, j, p.L, r16);
+    if constexpr (kKeepScores<D, G>) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sc[kt] = *reinterpret_cast<const f32x4*>(&sm.sc[lb][16 * kt + r16][0]);
+    } else {
+      block_scores<D>(sc, kf, qa, c2, j, p.L, r16);
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
