@@ -73,14 +73,17 @@ __device__ __forceinline__ int spin_flag(const int* flag, int* health) {
 }
 
 // Phase 1 keeps every block's scores in LDS for phase 3 (no K reload for kept
-// blocks) where that costs no occupancy: at d = 128 with G <= 4 the registers
-// already limit a CU to two work-groups, and 64 KB more LDS still fits two.
+// blocks) where that costs no occupancy: at d = 128 the registers already
+// limit a CU to two work-groups (G <= 4; 64 KB more LDS still fits two) or to
+// one (G = 8; 128 KB more still fits).
 template <int D, int G>
-constexpr bool kKeepScores = D == 128 && G <= 4;
+constexpr bool kKeepScores = D == 128;
+template <int G>
+constexpr int kScoreRows = G <= 4 ? 4 : 8;  // rows 4 q16 + i of lanes q16 < kScoreRows / 4
 
 template <int D, int G>
 struct DecSmem {
-  float sc[kKeepScores<D, G> ? 64 : 1][64][4];  // scores [block][key][row] (rows 0..3)
+  float sc[kKeepScores<D, G> ? 64 : 1][64][kScoreRows<G>];  // scores [block][key][row]
   float bm[64][G];              // block row maxima (log2 units)
   float m_ref[G];
   float lsum[4][G];
@@ -179,9 +182,9 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
       f32x4 acc[4];
       block_scores<D>(acc, kcur, qa, c2, blk0 + lb, p.L, r16);
       if constexpr (kKeepScores<D, G>) {
-        if (q16 == 0)  // rows 0..3: lanes 0..15 hold key 16 kt + lane
+        if (q16 < kScoreRows<G> / 4)  // rows 4 q16 .. 4 q16 + 3 of key 16 kt + r16
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f32x4*>(&sm.sc[lb][16 * kt + r16][0]) = acc[kt];
+          for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f32x4*>(&sm.sc[lb][16 * kt + r16][4 * q16]) = acc[kt];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -329,7 +332,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
     f32x4 sc[4];
     if constexpr (kKeepScores<D, G>) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sc[kt] = *reinterpret_cast<const f32x4*>(&sm.sc[lb][16 * kt + r16][0]);
+      for (int kt = 0; kt < 4; ++kt)  // lanes past the stored rows hold no row (row >= G): any stored value
+        sc[kt] = *reinterpret_cast<const f32x4*>(&sm.sc[lb][16 * kt + r16][4 * (q16 % (kScoreRows<G> / 4))]);
     } else {
       block_scores<D>(sc, kf, qa, c2, j, p.L, r16);
     }

@@ -75,7 +75,7 @@ def check_sequence(q, k, v, out, st, cnt, b, L, scale, lam, groups=None, order="
     return tot
 
 
-@pytest.mark.parametrize("G,d", [(4, 128), (1, 64), (2, 128), (8, 64)])
+@pytest.mark.parametrize("G,d", [(4, 128), (1, 64), (2, 128), (8, 64), (8, 128)])
 def test_decode_small_all_splits(G, d):
     Hkv = 2
     L = 3000                                   # ragged last block
