@@ -269,6 +269,15 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _index_tensor(t):
+    """A block-index array for the C ABI: an empty one (a CSR that keeps no
+    block) has no data pointer, so it is replaced by a one-element array the
+    kernels never read (row_ptr says there is nothing to read)."""
+    if t is None or t.numel() > 0:
+        return t
+    return _torch().zeros(1, dtype=t.dtype, device=t.device)
+
+
 class Plan:
     """A marshalled call: the C argument struct is built once; each call of the
     plan enqueues the operation on a stream (default: torch's current stream)
@@ -312,6 +321,7 @@ def prefill_plan(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, ca
     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d = B, Hq, Hkv, Nq, Nk, d
     for fld, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
         getattr(a, fld)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    col_idx = _index_tensor(col_idx)
     a.row_ptr, a.col_idx, a.tile_order = _ptr(row_ptr), _ptr(col_idx), _ptr(tile_order)
     a.n_valid = int(n_valid)
     a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
@@ -391,6 +401,7 @@ def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, 
         if t.dim() != 4 or t.stride(3) != 1:
             raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, f"{fld[:-7]} must be [B, N, H, d] with d contiguous")
         getattr(a, fld)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    col_idx, row_idx = _index_tensor(col_idx), _index_tensor(row_idx)
     a.row_ptr, a.col_idx, a.col_ptr, a.row_idx = _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx)
     a.n_valid = int(n_valid)
     a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))

@@ -88,7 +88,8 @@ def check_all(cfg, q, k, v, dout, csr=None, n_valid=None):
     rl = BW.prefill_lse(q, k, mask, cfg.scale)
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(lse), fin), "lse: rows with and without attended keys differ"
-    assert np.abs(lse[fin] - rl[fin]).max() <= LSE_ABS, f"lse max-abs {np.abs(lse[fin] - rl[fin]).max():.3e}"
+    if fin.any():
+        assert np.abs(lse[fin] - rl[fin]).max() <= LSE_ABS, f"lse max-abs {np.abs(lse[fin] - rl[fin]).max():.3e}"
     compare_grad(dq, rq, "dq")
     compare_grad(dk, rk, "dk")
     compare_grad(dv, rv, "dv")
@@ -227,3 +228,16 @@ def test_backward_after_skipping_forward(d):
     compare_grad(dq, rq, "dq")
     compare_grad(dk, rk, "dk")
     compare_grad(dv, rv, "dv")
+
+
+def test_empty_block_index():
+    """A CSR that keeps no block at all (an empty col_idx): the forward writes
+    zeros and lse = -inf, the backward zeros everywhere."""
+    cfg = _cfg(N=200, d=64, Hq=2, Hkv=1, seed=241)
+    _say("empty block index")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    csr = (np.zeros(3, np.int32), np.zeros(0, np.int32))
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr)
+    assert torch.all(out == 0) and np.all(np.isneginf(lse))
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
