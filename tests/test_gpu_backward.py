@@ -177,6 +177,35 @@ def test_backward_cfg2_full_size_sampled():
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_backward_causal_gqa_loaded(d):
+    """Causal GQA 32/8 at N 3072: enough work-groups to fill the GPU (the dQ
+    launch runs 768, the dK/dV launch 384), so the kernels run under the
+    contention of a real launch.  Every gradient of K/V head 5 and of its four
+    query heads against the oracle (dK and dV of a K/V head sum its query
+    heads only)."""
+    N, g = 3072, 5
+    cfg = PrefillWorkload(name="bwd_loaded", description="", dtype="bf16", B=1, Hq=32, Hkv=8, N=N, d=d, Br=128,
+                          Bc=64, causal=True, lam=0.0, mask=None, seed=251 + d, generator="iid")
+    _say(f"backward causal GQA 32/8 N{N} d{d}, K/V head {g}")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV))
+    mask = token_mask(N, None, N, True)
+    heads = list(range(4 * g, 4 * g + 4))
+    rk = np.zeros((N, d))
+    rv = np.zeros((N, d))
+    for h in heads:
+        hq, hk, hv = BW.masked_attention_grads(q[0, :, h], k[0, :, g], v[0, :, g], dout[0, :, h], mask, cfg.scale)
+        compare_grad(dq[0, :, h], hq, f"dq h{h}")
+        rk += hk
+        rv += hv
+        rl = BW.row_lse(q[0, :, h], k[0, :, g], mask, cfg.scale)
+        assert np.abs(lse[0, h] - rl).max() <= LSE_ABS
+    compare_grad(dk[0, :, g], rk, f"dk g{g}")
+    compare_grad(dv[0, :, g], rv, f"dv g{g}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_backward_after_skipping_forward(d):
     """BLASST forward (lambda > 0, causal GQA, the sink recipe so that blocks
     are skipped), then the backward with that forward's block_state: the
