@@ -512,6 +512,51 @@ def calibration_demo(target: float = 0.5, delta: float = 0.05):
 
 # ---------------------------------------------------------------------------- oracle on host cores
 
+def probe_peaks(steps: int = 20, warmup: int = 5):
+    """What this GPU reaches on plain library work, beside the published peaks
+    the rooflines use: a large bf16 GEMM (hipBLASLt through torch.matmul) for
+    the matrix cores, and memory-bound reductions and a copy over a few GB
+    for HBM (bytes moved per second; the copy counts its reads and writes)."""
+    import torch
+    out = {}
+
+    def best_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    for n in (8192, 16384):
+        a_ = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b_ = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        ms = best_ms(lambda: torch.matmul(a_, b_))
+        out[f"gemm_bf16_{n}_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a_, b_
+    torch.cuda.empty_cache()
+    nbytes = 8 << 30
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    rows = x.view(-1, 1 << 16)
+    ms = best_ms(lambda: rows.sum(dim=1, dtype=torch.float32))
+    out["read_sum_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    ms = best_ms(lambda: rows.amax(dim=1))
+    out["read_amax_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    half = x[: x.numel() // 2]
+    y = torch.empty_like(half)
+    ms = best_ms(lambda: y.copy_(half))
+    out["copy_read_plus_write_gbs"] = round(2 * half.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del x, y, half, rows
+    torch.cuda.empty_cache()
+    out["published_bf16_tflops"] = PEAK_BF16_TFLOPS
+    out["published_hbm_gbs"] = PEAK_HBM_GBS
+    return out
+
+
 def cpu_baseline_prefill(res, budget_s: float):
     """Time the float64 oracle (as it stands) on a bounded sample of the same
     workload's (batch, head, tile) items and extrapolate by processed blocks."""
@@ -573,6 +618,8 @@ def main(argv=None) -> int:
                     help="instead of the metric line: the static block-sparse backward on the prefill workloads")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the metric line: the decode order and decision variants on the decode workload")
+    ap.add_argument("--probe-peaks", action="store_true",
+                    help="instead of the metric line: what a large library GEMM and memory-bound reductions reach")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
@@ -608,6 +655,9 @@ def main(argv=None) -> int:
         names = [a.workload] + [n for n in (a.also.split(",") if a.also and not a.no_also else []) if n != "cfg5"]
         rep = [run_backward_workload(n, a.steps, a.warmup) for n in names]
         print(json.dumps({"backward": rep, "device": torch.cuda.get_device_name(0)}))
+        return 0
+    if a.probe_peaks:
+        print(json.dumps({"probe_peaks": probe_peaks(), "device": torch.cuda.get_device_name(0)}))
         return 0
     if a.variants:
         var = decode_variants("cfg5", [40.0 / 131072, 1e-2, 0.1], min(a.steps, 50), min(a.warmup, 20))
