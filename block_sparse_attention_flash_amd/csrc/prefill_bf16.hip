@@ -31,7 +31,8 @@
 // range-checked at the last key) into a two-stage ring, swizzled so that the
 // K-fragment reads and the V transpose reads are bank-conflict free; block
 // j+1 streams in during all of block j's work, and its block index is read
-// two blocks ahead.  One barrier per block (two when the vote is on).
+// two blocks ahead.  One barrier per block; the vote needs no second one
+// (a wave waits for the others' words only when its own rows all agree).
 // Several work-groups share a CU, so one group's exponentials overlap
 // another's MFMAs.
 //
@@ -80,7 +81,7 @@ template <int D>
 struct Smem {
   __bf16 k[kStages<D>][BC * D];
   __bf16 v[kStages<D>][BC * D];
-  int vote[2][4];
+  int vote[2][4];  // [0][w]: wave w's vote word on the current block; also scratch after the loop
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -326,6 +327,10 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   for (int n = 0; n < NTD; ++n) oacc[n] = f32x16{};
   int skipped = 0;
   int rows_agree = 0;  // row conditions that held (this wave's rows), for row_counters
+  if (DYN && !MAXONLY && tid < 4) {  // vote words: no block yet (the first block barrier orders this)
+    sm.vote[0][tid] = -1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
 
   constexpr int ST = kStages<D>;
   constexpr int DMA_PER_BLOCK = 2 * (D / 32);  // K and V loads of one block, per wave
@@ -432,11 +437,31 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       const bool wave_all = __all(agree);
       // lanes l and l + 32 hold the same row: count the wave's 32 rows once
       if (p.row_counters) rows_agree += __popcll(__ballot(agree && row_ok) & 0xffffffffull);
-      if (lane == 0) sm.vote[it & 1][wave] = wave_all ? 1 : 0;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the vote word is in LDS
-      block_barrier();
-      const int* vt = sm.vote[it & 1];
-      skip = (vt[0] & vt[1] & vt[2] & vt[3]) != 0;
+      // one word per wave: 2 it + (every row of the wave agrees).  A wave
+      // with a disagreeing row knows the block is kept and goes on; a wave
+      // whose rows all agree waits for the other waves' words on this block.
+      // Every wave writes its word before it can wait, and no wave passes
+      // the next block's barrier before all have finished this one (so a
+      // word is never overwritten while it is awaited): every wait ends.
+      if (lane == 0) sm.vote[0][wave] = 2 * it + (wave_all ? 1 : 0);
+      if (wave_all) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's word is in LDS
+        const volatile int* vt = sm.vote[0];
+        for (;;) {
+          int yes = 0, no = 0;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int x = vt[w];
+            yes += x == 2 * it + 1;
+            no += x == 2 * it;
+          }
+          if (no != 0 || yes == 4) {
+            skip = no == 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
     }
     if (p.block_state && tid == 0)
       p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = skip ? 2 : 1;
