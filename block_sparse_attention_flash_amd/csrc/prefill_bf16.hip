@@ -446,17 +446,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       if (lane == 0) sm.vote[0][wave] = 2 * it + (wave_all ? 1 : 0);
       if (wave_all) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's word is in LDS
-        const volatile int* vt = sm.vote[0];
+        const uint32_t yes = 2u * it + 1u;
         for (;;) {
-          int yes = 0, no = 0;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int x = vt[w];
-            yes += x == 2 * it + 1;
-            no += x == 2 * it;
-          }
-          if (no != 0 || yes == 4) {
-            skip = no == 0;
+          const u32x4 w = *reinterpret_cast<const volatile u32x4*>(sm.vote[0]);
+          if (w[0] == yes - 1 || w[1] == yes - 1 || w[2] == yes - 1 || w[3] == yes - 1) break;  // kept
+          if (w[0] == yes && w[1] == yes && w[2] == yes && w[3] == yes) {
+            skip = true;
             break;
           }
           __builtin_amdgcn_s_sleep(1);
