@@ -74,7 +74,7 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   w.ml = off;  off = align256(off + units * 128 * 2 * sizeof(float));
   w.cnt = off; off = align256(off + units * 2 * sizeof(int32_t));
   w.arrive = off; off = align256(off + units * sizeof(int32_t));  // n_merges <= n_slots
-  w.pre = off; off = align256(off + units * 128 * sizeof(float));
+  w.pre = off; off = align256(off + units * 128 * kPreSplit * sizeof(float));
   w.total = off;
   return w;
 }

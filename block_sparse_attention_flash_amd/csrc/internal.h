@@ -49,7 +49,7 @@ struct PrefillParams {
   float* part_ml;               // [n_slots][B][Hq][128][2]  (reference max in raw score units, row sum)
   int32_t* part_cnt;            // [n_slots][B][Hq][2]
   int32_t* arrive;              // [n_merges][B][Hq] chunk arrival counters (zero between calls)
-  float* part_pre;              // [n_slots][B][Hq][128] lambda > 0: per-row max of each chunk
+  float* part_pre;              // [n_slots][B][Hq][kPreSplit][128] lambda > 0: per-row max of each share of a chunk
   int32_t rank_major;           // bf16 kernel: XCD work order (set by its launcher)
   float* lse;                   // optional [B][Hq][Nq] natural-log row sums of exp
 };
@@ -86,6 +86,10 @@ struct BwdParams {
 };
 
 int launch_prefill_bwd(const BwdParams& p, void* stream);
+
+// Work-groups per chunk of a cut tile in the chunk-maximum pass (each takes
+// an equal share of the chunk's blocks and keeps its own row maxima).
+constexpr int kPreSplit = 8;
 
 struct PrefillWorkspace {
   size_t o, ml, cnt, arrive, pre, total;

@@ -216,8 +216,18 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const int units = p.sched_items ? p.n_items : p.Tr;
   const int G = p.Hq / p.Hkv;
   const int NBG = p.B * p.Hkv;
-  int hh, rank, bg;
-  if ((NBG & 7) == 0) {
+  int hh, rank = 0, bg, sub = 0;
+  if (MAXONLY) {
+    // grid: (slot, batch, head, kPreSplit sub-ranges), sub-range fastest
+    int64_t k = blockIdx.x;
+    sub = (int)(k % kPreSplit);
+    k /= kPreSplit;
+    const int h0 = (int)(k % p.Hq);
+    k /= p.Hq;
+    hh = h0 % G;
+    bg = (int)(k % p.B) * p.Hkv + h0 / G;
+    rank = (int)(k / p.B);  // the slot
+  } else if ((NBG & 7) == 0) {
     const int per = NBG >> 3;
     int64_t k = blockIdx.x >> 3;
     hh = (int)(k % G);
@@ -240,7 +250,23 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   const int b = bg / p.Hkv;
   const int h = g * G + hh;
   int t, e0, e1, slot = -1, mrg = -1;
-  if (p.sched_items) {
+  if (MAXONLY) {
+    // chunk `slot` of a cut tile: its merge (slots are numbered merge by
+    // merge, so the merge is the last one starting at or below the slot),
+    // and its block range, cut exactly as the schedule builder cuts it
+    slot = rank;
+    int lo = 0, hi_m = p.n_merges;
+    while (hi_m - lo > 1) {
+      const int mid = (lo + hi_m) >> 1;
+      if (p.sched_merges[3 * mid + 1] <= slot) lo = mid; else hi_m = mid;
+    }
+    mrg = lo;
+    t = p.sched_merges[3 * mrg];
+    const int c = slot - p.sched_merges[3 * mrg + 1], ns = p.sched_merges[3 * mrg + 2];
+    const int rb = p.row_ptr[t], n = p.row_ptr[t + 1] - rb;
+    e0 = rb + (int)((int64_t)n * c / ns);
+    e1 = rb + (int)((int64_t)n * (c + 1) / ns);
+  } else if (p.sched_items) {
     const int32_t* item = p.sched_items + 5 * rank;
     t = item[0];
     e0 = item[1];
@@ -259,7 +285,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   e1 = __builtin_amdgcn_readfirstlane(e1);
   slot = __builtin_amdgcn_readfirstlane(slot);
   mrg = __builtin_amdgcn_readfirstlane(mrg);
-  if (MAXONLY && slot < 0) return;  // only chunks of cut tiles need their maxima
+  if constexpr (MAXONLY) {
+    // the chunk visited last (ascending: the highest slot; descending: the
+    // lowest) has no later chunk that reads its maxima
+    const int s0 = p.sched_merges[3 * mrg + 1], ns = p.sched_merges[3 * mrg + 2];
+    if (slot == (p.block_order ? s0 : s0 + ns - 1)) return;
+  }
 
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
@@ -295,7 +326,15 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       nblk = max(0, min(nblk, last_row / BC + 1 - e0));
     }
   }
+  // MAXONLY: this work-group's share of the chunk, visiting positions
+  // [first, first + nblk) (order does not matter for a maximum)
+  int first = 0;
+  if (MAXONLY) {
+    first = (int)((int64_t)nblk * sub / kPreSplit);
+    nblk = (int)((int64_t)nblk * (sub + 1) / kPreSplit) - first;
+  }
   nblk = __builtin_amdgcn_readfirstlane(nblk);
+  first = __builtin_amdgcn_readfirstlane(first);
 
   const float c2 = p.scale * kLog2e;                    // raw score -> log2 units
   const float log2_lambda = DYN ? log2f(p.lambda) : kNegInf;
@@ -307,7 +346,9 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     const int ns = p.sched_merges[3 * mrg + 2];
     const int lo = p.block_order ? slot + 1 : s0, hi_s = p.block_order ? s0 + ns : slot;
     for (int sl = lo; sl < hi_s; ++sl)
-      m_run = fmaxf(m_run, p.part_pre[(((int64_t)sl * p.B + b) * p.Hq + h) * BR + wave * 32 + l32]);
+#pragma unroll
+      for (int q = 0; q < kPreSplit; ++q)
+        m_run = fmaxf(m_run, p.part_pre[((((int64_t)sl * p.B + b) * p.Hq + h) * kPreSplit + q) * BR + wave * 32 + l32]);
   }
   float m_chunk = kNegInf;  // MAXONLY: this row's maximum over the chunk
   float m_ref = kNegInf;   // reference max used in the exponent (raw units)
@@ -339,9 +380,9 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const const_i32_ptr ccols = cols ? (const_i32_ptr)(cols) : nullptr;
   // visiting position i -> key block: ascending, or descending (most recent keys first)
-  const bool desc = p.block_order != 0;
+  const bool desc = !MAXONLY && p.block_order != 0;
   auto blk = [&](int i) __attribute__((always_inline)) {
-    const int e = desc ? nblk - 1 - i : i;
+    const int e = desc ? nblk - 1 - i : first + i;
     return i < nblk ? (ccols ? ccols[e] : e0 + e) : 0;
   };
   TileSrc<D, false> ksrc;
@@ -525,7 +566,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     else q2 = blk(it + 3);
   }
   if constexpr (MAXONLY) {
-    if (hi == 0) p.part_pre[(((int64_t)slot * p.B + b) * p.Hq + h) * BR + wave * 32 + l32] = m_chunk;
+    if (hi == 0) p.part_pre[((((int64_t)slot * p.B + b) * p.Hq + h) * kPreSplit + sub) * BR + wave * 32 + l32] = m_chunk;
     return;
   }
   float l_tot;
@@ -659,8 +700,9 @@ hipError_t launch(const PrefillParams& p0, hipStream_t s) {
   const int64_t grid = (int64_t)p.B * p.Hq * units;
   // rank-major when one XCD (32 CUs) has under four waves of work-groups
   p.rank_major = grid / 8 < 4 * 32 * kMinBlocksPerCu<D> ? 1 : 0;
-  if (DYN && p.n_slots > 0) {  // cut tiles: the chunk maxima first (same grid, uncut items return)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, true>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+  if (DYN && p.n_slots > 0) {  // cut tiles: the chunk maxima first, kPreSplit work-groups per chunk and head
+    const int64_t pre_grid = (int64_t)p.n_slots * p.B * p.Hq * kPreSplit;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, true>), dim3((unsigned)pre_grid), dim3(NT), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

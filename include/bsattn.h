@@ -171,7 +171,12 @@ bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t*
  *                        directly, else merge indexes `merges`; items are
  *                        ordered longest first
  *   merges [n_merges][3] {tile, first slot, number of slots}; the slots of a
- *                        cut tile are consecutive
+ *                        cut tile are consecutive, and chunk c of k covers
+ *                        the tile's CSR entries [f + n c / k, f + n (c + 1) / k)
+ *                        (f its first entry, n its count; integer division):
+ *                        the chunk-maximum pass (lambda > 0) takes the
+ *                        ranges from this rule, so a hand-made schedule must
+ *                        cut the same way
  * Two-call pattern: items == NULL returns the counts only.  Host buffers.
  * max_blocks_per_item >= 1.  Returns BSATTN_ERR_CAPACITY if a buffer is short.
  */
