@@ -104,6 +104,11 @@ __device__ __forceinline__ bf16x8 read_tr(const __bf16* tile, int r0, int n, int
                      lds_read_tr16(tile + BTile<D>::pos(r + 8, c) + half));
 }
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr_b(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(ptr);
+}
+
 // Dv = rowsum(dout * out), fp32, one row per D/8 lanes.
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_dot_kernel(const BwdParams p) {
@@ -325,6 +330,329 @@ __global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const
 #endif
 }
 
+// ---- dK/dV at d = 128: key-block pairs, double-buffered query stages --------
+//
+// The kernel above keeps one 64-row query stage in LDS and waits for each
+// stage's load before computing on it: at d = 128 two work-groups fill a
+// CU's LDS, so the load latency of every stage is exposed to the MFMAs of
+// only one other work-group.  Here one work-group of eight waves takes two
+// adjacent key blocks (2m, 2m + 1), so their K/V (64 KB) and two 64-row
+// query stages (64 KB) fit one CU: the next stage streams in while the
+// current one is computed, behind a single barrier per stage.  Waves 4 kb ..
+// 4 kb + 3 work on block 2m + kb exactly as the four waves above do; the
+// stages visited are those of either block (the union of the two tiles'
+// lists, or the shared causal range), and a block's waves sit out stages that
+// do not touch it.  The Q / dO stages' transposed reads are inline asm that
+// waits inside the block: the intrinsic would make the compiler wait for
+// the next stage's load first (it cannot tell the stages apart).
+
+constexpr int NT2 = 512;
+
+template <int D>
+struct Dkdv2Smem {
+  __bf16 k[2][BC * D];  // keys of blocks 2m, 2m + 1
+  __bf16 v[2][BC * D];
+  __bf16 q[2][64 * D];  // double-buffered 64-row query stages
+  __bf16 g[2][64 * D];  // their dout
+  float lse[2][64];     // per stage: lse (natural log) and Dv of its rows
+  float dvec[2][64];
+};
+
+// 64 x D tile, global -> LDS, by all eight waves (rows past rows_total: zeros).
+template <int D>
+__device__ __forceinline__ void dma_tile64_w8(__bf16* tile, const __bf16* head, int rows_total, int64_t stride_t,
+                                              int row0, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int NI = 64 * CH / NT2;
+  const uint32_t extent = (uint32_t)(((int64_t)(rows_total - 1) * stride_t + D) * 2);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, (int)extent, kBufferWord3);
+  const uint32_t soff = (uint32_t)((int64_t)row0 * stride_t * 2);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (8 * i + wave) * 64 + lane;
+    const int r = slot / CH, cp = slot % CH;
+    const int c = cp ^ BTile<D>::swz(r);
+    const uint32_t voff = (uint32_t)(((int64_t)r * stride_t + 8 * c) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (8 * i + wave) * 64 * 8), 16, voff, soff, 0, 0);
+  }
+}
+
+// 64 consecutive floats of a row vector (rows row0 .. row0 + 63 of a [.., N]
+// float array, zeros past n_total), global -> LDS by one wave.
+__device__ __forceinline__ void dma_row64(float* dst, const float* src_row, int n_total, int row0, int lane) {
+  const uint32_t extent = (uint32_t)n_total * 4;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src_row), (short)0, (int)extent, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, (uint32_t)lane * 4, (uint32_t)row0 * 4, 0, 0);
+}
+
+// The four d-tiles' transposed fragments of one 16-row step (read_tr for
+// n = 0..3), issued together and waited for inside the asm block.  The
+// loads return into their registers some cycles after the block issues
+// them, which the compiler does not see: `busy` (the operands of the MFMAs
+// issued just before, which may not have read them yet) are inputs of the
+// block, so its outputs (early-clobber) are never placed on top of them.
+__device__ __forceinline__ void read_tr_x4(bf16x8 (&out)[4], const __bf16* tile, int r0, int lane,
+                                           const bf16x8 (&busy)[4], const bf16x8& busy_b) {
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int r = r0 + 4 * (g16 >> 1) + (j16 >> 2);
+  const int half = 4 * (j16 & 1);
+  uint32_t a[8];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int c = 4 * n + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    a[2 * n] = lds_addr_b(tile + BTile<128>::pos(r, c) + half);
+    a[2 * n + 1] = lds_addr_b(tile + BTile<128>::pos(r + 8, c) + half);
+  }
+  i16x4 x[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %9\n"
+      "ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n"
+      "ds_read_b64_tr_b16 %4, %12\n"
+      "ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n"
+      "ds_read_b64_tr_b16 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(busy[0]),
+        "v"(busy[1]), "v"(busy[2]), "v"(busy[3]), "v"(busy_b)
+      : "memory");
+#pragma unroll
+  for (int n = 0; n < 4; ++n) out[n] = join_bf16x4(x[2 * n], x[2 * n + 1]);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  constexpr int KS = D / 16;
+  constexpr int NTD = D / 32;
+  __shared__ Dkdv2Smem<D> sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int kb = wave >> 2, kh = wave & 1, qh = (wave >> 1) & 1;
+  // work order as above: key-block pairs ascending, (batch, K/V head) fastest
+  const int NBG = p.B * p.Hkv;
+  const int m = blockIdx.x / NBG;
+  const int bg = blockIdx.x % NBG;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const float c2 = p.scale * kLog2e;
+  const int j0 = 2 * m;
+  const bool has1 = j0 + 1 < p.Tc;
+  const int jw = j0 + kb;  // this wave's block
+
+  const int key = jw * BC + 32 * kh + l32;
+  const bool key_ok = key < p.n_valid;
+  const __bf16* kh_base = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vh_base = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
+  dma_tile64_w8<D>(sm.k[0], kh_base, p.Nk, p.ks_t, j0 * BC, wave, lane);
+  dma_tile64_w8<D>(sm.v[0], vh_base, p.Nk, p.vs_t, j0 * BC, wave, lane);
+  if (has1) {
+    dma_tile64_w8<D>(sm.k[1], kh_base, p.Nk, p.ks_t, (j0 + 1) * BC, wave, lane);
+    dma_tile64_w8<D>(sm.v[1], vh_base, p.Nk, p.vs_t, (j0 + 1) * BC, wave, lane);
+  }
+
+  // the stages: for each query head of the group, the tiles holding either
+  // block (merge of the two transposed lists, or the causal / dense range
+  // shared by the pair), two 64-row halves each; a stage is kept when it
+  // touches a block (not past the last row, not wholly above the block's
+  // first key, not a block the forward skipped for that head and tile)
+  // the transposed index through the scalar cache (wave-uniform, read-only)
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr rowi = p.row_idx ? (const_i32_ptr)p.row_idx : nullptr;
+  int b0 = 0, n0 = 0, b1 = 0, n1 = 0, tlo = 0;
+  if (p.col_ptr) {
+    b0 = p.col_ptr[j0];
+    n0 = p.col_ptr[j0 + 1] - b0;
+    if (has1) {
+      b1 = p.col_ptr[j0 + 1];
+      n1 = p.col_ptr[j0 + 2] - b1;
+    }
+  } else {
+    tlo = CAUSAL ? (j0 * BC) / BR : 0;  // both blocks of the pair start at this tile
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  b1 = __builtin_amdgcn_readfirstlane(b1);
+  n1 = __builtin_amdgcn_readfirstlane(n1);
+  // cursor: head index hc, list positions (i0, i1) or tile tc, half hf
+  struct Cur {
+    int hc, i0, i1, tc, hf;
+  };
+  auto touches = [&](int h, int t, int hf, int jb) __attribute__((always_inline)) {
+    const int row0 = t * BR + 64 * hf;
+    if (jb >= p.Tc || row0 >= p.Nq) return false;
+    if (CAUSAL && row0 + 63 < jb * BC) return false;
+    if (p.block_state && p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + jb] == 2) return false;
+    return true;
+  };
+  // tile at the cursor and which blocks' lists hold it (-1: head exhausted)
+  auto tile_at = [&](const Cur& c, bool& in0, bool& in1) __attribute__((always_inline)) {
+    if (p.col_ptr) {
+      const int t0 = c.i0 < n0 ? rowi[b0 + c.i0] : INT32_MAX;
+      const int t1 = c.i1 < n1 ? rowi[b1 + c.i1] : INT32_MAX;
+      const int t = min(t0, t1);
+      in0 = t0 == t;
+      in1 = t1 == t;
+      return t == INT32_MAX ? -1 : t;
+    }
+    in0 = true;
+    in1 = has1;
+    return c.tc < p.Tr ? c.tc : -1;
+  };
+  auto step = [&](Cur& c) __attribute__((always_inline)) {  // to the next (tile, half) position
+    bool in0, in1;
+    if (c.hf == 0) {
+      c.hf = 1;
+      return;
+    }
+    c.hf = 0;
+    if (p.col_ptr) {
+      tile_at(c, in0, in1);
+      c.i0 += in0 ? 1 : 0;
+      c.i1 += in1 ? 1 : 0;
+    } else {
+      ++c.tc;
+    }
+  };
+  // advance c to the first kept stage at or after it; false when none is left
+  auto settle = [&](Cur& c, int& t, int& need) __attribute__((always_inline)) {
+    for (;;) {
+      if (c.hc >= G) return false;
+      bool in0, in1;
+      t = tile_at(c, in0, in1);
+      if (t < 0) {  // next head
+        c = Cur{c.hc + 1, 0, 0, tlo, 0};
+        continue;
+      }
+      const int h = g * G + c.hc;
+      need = (in0 && touches(h, t, c.hf, j0) ? 1 : 0) | (in1 && touches(h, t, c.hf, j0 + 1) ? 2 : 0);
+      if (need) return true;
+      step(c);
+    }
+  };
+  auto fetch = [&](int buf, int h, int t, int hf) __attribute__((always_inline)) {
+    const int row0 = t * BR + 64 * hf;
+    dma_tile64_w8<D>(sm.q[buf], static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h, p.Nq,
+                     p.qs_t, row0, wave, lane);
+    dma_tile64_w8<D>(sm.g[buf], static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h,
+                     p.Nq, p.dos_t, row0, wave, lane);
+    const int64_t rb = ((int64_t)b * p.Hq + h) * p.Nq;
+    if (wave == 0) dma_row64(sm.lse[buf], p.lse + rb, p.Nq, row0, lane);
+    if (wave == 1) dma_row64(sm.dvec[buf], p.dvec + rb, p.Nq, row0, lane);
+  };
+
+  f32x16 dk[NTD], dv[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
+
+  Cur cur{0, 0, 0, tlo, 0};
+  int t_cur = 0, need_cur = 0;
+  bool have = settle(cur, t_cur, need_cur);
+  if (have) fetch(0, g * G + cur.hc, t_cur, cur.hf);
+  for (int st = 0; have; ++st) {
+    const int buf = st & 1;
+    // this stage (and, the first time, K and V) has landed in every wave, and
+    // every wave is done with the previous stage, whose buffers are next
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const int h = g * G + cur.hc, t = t_cur, hf = cur.hf, need = need_cur;
+    Cur nxt = cur;
+    step(nxt);
+    int t_nxt = 0, need_nxt = 0;
+    const bool have_nxt = settle(nxt, t_nxt, need_nxt);
+    if (have_nxt) fetch(buf ^ 1, g * G + nxt.hc, t_nxt, nxt.hf);
+
+    if ((need >> kb) & 1) {
+      const int row0 = t * BR + 64 * hf;
+      const int nrows = min(64, p.Nq - row0);
+      const int r0 = 32 * qh;
+      const __bf16* sq = sm.q[buf];
+      const __bf16* sg = sm.g[buf];
+      f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 frg[4], frq[4], dbp = bf16x8{};
+#pragma unroll
+      for (int n = 0; n < 4; ++n) frq[n] = bf16x8{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(read_row<D>(sq, r0 + l32, ks, hi), read_row<D>(sm.k[kb], 32 * kh + l32, ks, hi), s);
+        dp = mfma32(read_row<D>(sg, r0 + l32, ks, hi), read_row<D>(sm.v[kb], 32 * kh + l32, ks, hi), dp);
+        if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int a = 8 * kk + i;
+          const int rl = r0 + 8 * (a >> 2) + 4 * hi + (a & 3);
+          const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
+          pv[i] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse[buf][rl] * kLog2e)) : 0.0f;
+          dsv[i] = pv[i] * (dp[a] - sm.dvec[buf][rl]);
+        }
+        const bf16x8 pb = to_bf16x8(pv);
+        const bf16x8 db = to_bf16x8(dsv);
+        // (the first read follows the dK products of the previous step; the
+        // S and dP products before the first step have been waited for)
+        read_tr_x4(frg, sg, r0 + 16 * kk, lane, frq, dbp);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) dv[n] = mfma32(frg[n], pb, dv[n]);  // dV^T += dO^T P
+        read_tr_x4(frq, sq, r0 + 16 * kk, lane, frg, pb);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) dk[n] = mfma32(frq[n], db, dk[n]);  // dK^T += Q^T dS
+        dbp = db;
+      }
+    }
+    cur = nxt;
+    t_cur = t_nxt;
+    need_cur = need_nxt;
+    have = have_nxt;
+  }
+
+  // each block's row halves: waves with qh = 1 hand their sums to the waves
+  // with qh = 0 through LDS (free once every wave is past its last stage)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  static_assert(sizeof(float) * 4 * 2 * NTD * 16 * 64 <= sizeof(Dkdv2Smem<D>), "reduction fits in the tiles");
+  float* red = reinterpret_cast<float*>(&sm) + (2 * kb + kh) * (2 * NTD * 16 * 64);
+  if (qh == 1) {
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        red[(n * 16 + a) * 64 + lane] = dk[n][a];
+        red[((NTD + n) * 16 + a) * 64 + lane] = dv[n][a];
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && jw < p.Tc && key < p.Nk) {
+    __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
+    __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        dk[n][a] += red[(n * 16 + a) * 64 + lane];
+        dv[n][a] += red[((NTD + n) * 16 + a) * 64 + lane];
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dcol = 32 * n + 8 * q4 + 4 * hi;
+        store4(dkp + dcol, dk[n], q4, p.scale);
+        store4(dvp + dcol, dv[n], q4, 1.0f);
+      }
+    }
+  }
+#endif
+}
+
 template <int D>
 struct DqSmem {
   __bf16 k[BC * D];
@@ -451,7 +779,11 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)dot_blocks), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.Tc)), dim3(NT), 0, s, p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * ((p.Tc + 1) / 2))),
+                       dim3(NT2), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.Tc)), dim3(NT), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
   return hipGetLastError();
