@@ -132,9 +132,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
 // address for d tile n at key step 0; step kk adds 32 kk D bytes, the upper
 // 8 keys 16 D bytes.  (The intrinsic form makes the compiler wait for every
 // pending global->LDS load first: it cannot tell the V stage from the stage
-// being filled.)
+// being filled.)  The loads return into their registers after the block has
+// issued them, which the compiler does not see, while MFMAs issued just
+// before may not have read their operands yet: those operands (`busy`, the
+// previous step's fragments and P) are inputs of the block, so its outputs
+// (early-clobber) are never placed on top of them.
 template <int D, int KK>
-__device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t (&base)[D / 32]) {
+__device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t (&base)[D / 32],
+                                            const bf16x8 (&busy)[D / 32], const bf16x8& busy_p) {
   constexpr int O0 = 32 * KK * D, O1 = 32 * KK * D + 16 * D;
   i16x4 x[2 * (D / 32)];
   if constexpr (D == 64) {
@@ -144,8 +149,8 @@ __device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t
         "ds_read_b64_tr_b16 %2, %5 offset:%c6\n"
         "ds_read_b64_tr_b16 %3, %5 offset:%c7\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3])
-        : "v"(base[0]), "v"(base[1]), "i"(O0), "i"(O1)
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(base[0]), "v"(base[1]), "i"(O0), "i"(O1), "v"(busy[0]), "v"(busy[1]), "v"(busy_p)
         : "memory");
   } else {
     asm volatile(
@@ -158,8 +163,9 @@ __device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t
         "ds_read_b64_tr_b16 %6, %11 offset:%c12\n"
         "ds_read_b64_tr_b16 %7, %11 offset:%c13\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
-        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(O0), "i"(O1)
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(O0), "i"(O1), "v"(busy[0]), "v"(busy[1]),
+          "v"(busy[2]), "v"(busy[3]), "v"(busy_p)
         : "memory");
   }
 #pragma unroll
@@ -540,22 +546,27 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       uint32_t vb[NTD];
 #pragma unroll
       for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
-      bf16x8 vf[NTD];
-      read_v_step<D, 0>(vf, vb);
+      // two fragment sets in turn: a step's loads never land on the operands
+      // of the previous step's products (before the first step, the QK^T
+      // products have been waited for: the exponentials used their results)
+      bf16x8 va[NTD], vb2[NTD];
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[0], oacc[n]);
+      for (int n = 0; n < NTD; ++n) vb2[n] = bf16x8{};
+      read_v_step<D, 0>(va, vb, vb2, pf[3]);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[0], oacc[n]);
       if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[0], lacc);
-      read_v_step<D, 1>(vf, vb);
+      read_v_step<D, 1>(vb2, vb, va, pf[0]);
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[1], oacc[n]);
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[1], oacc[n]);
       if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[1], lacc);
-      read_v_step<D, 2>(vf, vb);
+      read_v_step<D, 2>(va, vb, vb2, pf[1]);
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[2], oacc[n]);
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[2], oacc[n]);
       if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[2], lacc);
-      read_v_step<D, 3>(vf, vb);
+      read_v_step<D, 3>(vb2, vb, va, pf[2]);
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vf[n], pf[3], oacc[n]);
+      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[3], oacc[n]);
       if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[3], lacc);
     } else {
       ++skipped;
