@@ -772,6 +772,130 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
 #endif
 }
 
+// dQ at d = 128 with the key blocks streamed global -> LDS by DMA into two
+// stages (the kernel above reads the next block into registers and copies
+// it to LDS between two barriers): block e + 1 lands while block e is
+// computed, behind one barrier per block.  The transposed reads are asm
+// blocks under the same rule as in the dK/dV pair kernel.
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  constexpr int KS = D / 16;
+  constexpr int NTD = D / 32;
+  __shared__ __bf16 smk[2][BC * D];
+  __shared__ __bf16 smv[2][BC * D];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  // work order as above
+  const int G = p.Hq / p.Hkv;
+  const int NBG = p.B * p.Hkv;
+  const int bg = blockIdx.x % NBG;
+  const int hh = (blockIdx.x / NBG) % G;
+  const int rank = blockIdx.x / (NBG * G);
+  const int t = CAUSAL ? p.Tr - 1 - rank : rank;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int h = g * G + hh;
+  const float c2 = p.scale * kLog2e;
+
+  const int row = t * BR + wave * 32 + l32;
+  const bool row_ok = row < p.Nq;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)row * p.qs_t + (int64_t)h * p.qs_h;
+  const __bf16* grow =
+      static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)row * p.dos_t + (int64_t)h * p.dos_h;
+  bf16x8 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hi) : bf16x8{};
+    gf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(grow + 16 * ks + 8 * hi) : bf16x8{};
+  }
+  const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + row;
+  const float lse2 = row_ok ? p.lse[ri] * kLog2e : 0.0f;
+  const float dvr = row_ok ? p.dvec[ri] : 0.0f;
+
+  const int last_row = min(t * BR + BR, p.Nq) - 1;
+  int e0 = p.row_ptr ? p.row_ptr[t] : 0;
+  int e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
+  if (CAUSAL) {
+    if (p.row_ptr) {
+      while (e1 > e0 && p.col_idx[e1 - 1] * BC > last_row) --e1;
+    } else {
+      e1 = min(e1, last_row / BC + 1);
+    }
+  }
+  e0 = __builtin_amdgcn_readfirstlane(e0);
+  e1 = __builtin_amdgcn_readfirstlane(e1);
+
+  // block indices through the scalar cache, one iteration ahead
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr cols = p.col_idx ? (const_i32_ptr)p.col_idx : nullptr;
+  auto blk = [&](int e) __attribute__((always_inline)) { return e < e1 ? (cols ? cols[e] : e) : 0; };
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
+  auto fetch = [&](int buf, int j) __attribute__((always_inline)) {
+    dma_tile64<D>(smk[buf], kbase, p.Nk, p.ks_t, j * BC, wave, lane);
+    dma_tile64<D>(smv[buf], vbase, p.Nk, p.vs_t, j * BC, wave, lane);
+  };
+  f32x16 dq[NTD];
+#pragma unroll
+  for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
+
+  const uint8_t* skipped = p.block_state ? p.block_state + (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc : nullptr;
+  int j = blk(e0), jn = blk(e0 + 1);
+  if (e0 < e1) fetch(0, j);
+  bf16x8 fa[4], fb[4], dbp = bf16x8{};
+#pragma unroll
+  for (int n = 0; n < 4; ++n) fb[n] = bf16x8{};
+  for (int e = e0; e < e1; ++e) {
+    const int buf = (e - e0) & 1;
+    // block e has landed in every wave, and every wave is done with block e - 1
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (e + 1 < e1) fetch(buf ^ 1, jn);
+    const int jc = j;
+    j = jn;
+    jn = blk(e + 2);
+    if (skipped && skipped[jc] == 2) continue;  // the forward skipped it: no gradient (uniform branch)
+    const __bf16* sk = smk[buf];
+    const __bf16* sv = smv[buf];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(read_row<D>(sk, 32 * mt + l32, ks, hi), qf[ks], s);   // S^T[key][q]
+        dp = mfma32(read_row<D>(sv, 32 * mt + l32, ks, hi), gf[ks], dp);  // dP^T[key][q]
+      }
+      float dsv[16];
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = jc * BC + 32 * mt + 8 * (a >> 2) + 4 * hi + (a & 3);
+        const bool ok = row_ok && key < p.n_valid && (!CAUSAL || key <= row);
+        const float pr = ok ? fast_exp2(fmaf(s[a], c2, -lse2)) : 0.0f;
+        dsv[a] = pr * (dp[a] - dvr);
+      }
+      const bf16x8 d0 = to_bf16x8(dsv), d1 = to_bf16x8(dsv + 8);
+      read_tr_x4(fa, sk, 32 * mt, lane, fb, dbp);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fa[n], d0, dq[n]);
+      read_tr_x4(fb, sk, 32 * mt + 16, lane, fa, d0);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fb[n], d1, dq[n]);
+      dbp = d1;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (row_ok) {
+    __bf16* dqp = static_cast<__bf16*>(p.dq) + (int64_t)b * p.dqs_b + (int64_t)row * p.dqs_t + (int64_t)h * p.dqs_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) store4(dqp + 32 * n + 8 * q4 + 4 * hi, dq[n], q4, p.scale);
+  }
+#endif
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
@@ -785,7 +909,10 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.Tc)), dim3(NT), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dq_db_kernel<CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
