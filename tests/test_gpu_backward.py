@@ -155,6 +155,22 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_deterministic_under_full_load(d):
+    """The backward at a shape that fills the GPU (causal GQA 32/8, N 4096),
+    three runs, bit-identical gradients (see the forward's test of the same
+    name)."""
+    cfg = PrefillWorkload(name="bwd_det", description="", dtype="bf16", B=1, Hq=32, Hkv=8, N=4096, d=d, Br=128,
+                          Bc=64, causal=True, lam=0.0, mask=None, seed=261 + d, generator="iid")
+    _say(f"backward determinism under load d{d}")
+    q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+    dout = gen_prefill_grad_output(cfg).to(DEV)
+    runs = [run_fwd_bwd(cfg, q, k, v, dout) for _ in range(3)]
+    for r in runs[1:]:
+        for x, y in zip(r[2:], runs[0][2:]):
+            assert torch.equal(x, y)
+
+
 def test_backward_cfg2_full_size_sampled():
     """The DiT image+text workload at full size (B 2, H 16, N 4352, d 64):
     every gradient of two (batch, head) pairs against the oracle run on that

@@ -202,6 +202,31 @@ def test_deterministic_repeat():
     assert torch.equal(o1, o2) and np.array_equal(s1, s2) and np.array_equal(c1, c2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_deterministic_under_full_load(d):
+    """Timing-dependent faults (a load landing on an operand a queued MFMA
+    has not read, a missing wait) show as run-to-run differences: the full
+    DiT image+text shape (d 64) and a causal GQA 32/8 shape at N 8192
+    (d 128), with and without BLASST, five launches each, bit-identical."""
+    if d == 64:
+        cfg = get_config("cfg2")
+        q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+        rp, ci = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+        kw = dict(row_ptr=torch.from_numpy(rp).to(DEV), col_idx=torch.from_numpy(ci).to(DEV))
+        causal = False
+    else:
+        cfg = _small("loaded", N=8192, d=128, Hq=32, Hkv=8, B=1, causal=True, generator="concentrated")
+        q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+        kw = {}
+        causal = True
+    for lam in (0.0, 0.3):
+        _say(f"determinism under load: d{d} lambda {lam}")
+        outs = [bsa.prefill_fwd(q, k, v, scale=cfg.scale, causal=causal, lam=lam, **kw) for _ in range(5)]
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
+
+
 def test_strided_views():
     """q/k/v as non-contiguous views of a packed [B, N, 3, H, d] tensor, output into a strided view."""
     B, N, H, d = 1, 260, 2, 64
