@@ -547,12 +547,16 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 #pragma unroll
       for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
       // two fragment sets in turn: a step's loads never land on the operands
-      // of the previous step's products (before the first step, the QK^T
-      // products have been waited for: the exponentials used their results)
+      // of the previous step's products.  Before the first step no product is
+      // in flight: the block row max waited for the last QK^T product, and the
+      // matrix pipe runs a wave's products in order.
       bf16x8 va[NTD], vb2[NTD];
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) vb2[n] = bf16x8{};
-      read_v_step<D, 0>(va, vb, vb2, pf[3]);
+      if constexpr (NTD == 4) {
+        read_v_step<D, 0>(va, vb, pf, pf[3]);  // (the P fragments: live anyway, nothing to protect)
+      } else {
+        const bf16x8 live[NTD] = {pf[2], pf[3]};
+        read_v_step<D, 0>(va, vb, live, pf[1]);
+      }
 #pragma unroll
       for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[0], oacc[n]);
       if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[0], lacc);
