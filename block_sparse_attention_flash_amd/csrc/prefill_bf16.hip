@@ -13,7 +13,10 @@
 //                ballot, one LDS word per wave, as in notes section 4)
 //   if kept:     P = 2^(S*scale*log2e - m),  l += rowsum(P),
 //                O^T += V^T P^T  (V read transposed from LDS with
-//                ds_read_b64_tr_b16)
+//                ds_read_b64_tr_b16: at d = 128 one key step at a time,
+//                each step's reads under the previous step's products; at
+//                d = 64 without the vote, all four steps at once under the
+//                QK^T products)
 //
 // Layout choice: computing S^T (keys x rows) puts one query row per lane
 // (row = lane % 32, split over lanes l and l+32), so the row max, the row
@@ -170,6 +173,37 @@ __device__ __forceinline__ void read_v_step(bf16x8 (&vf)[D / 32], const uint32_t
   }
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) vf[n] = join_bf16x4(x[2 * n], x[2 * n + 1]);
+}
+
+// d = 64: all four key steps' V fragments in one block of reads, issued
+// while the QK^T products run (busy: the K fragments those products read).
+__device__ __forceinline__ void read_v_all64(bf16x8 (&vf)[4][2], const uint32_t (&base)[2], const bf16x8 (&busy)[4]) {
+  i16x4 x[16];
+  asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:0\n"
+        "ds_read_b64_tr_b16 %1, %16 offset:1024\n"
+        "ds_read_b64_tr_b16 %2, %17 offset:0\n"
+        "ds_read_b64_tr_b16 %3, %17 offset:1024\n"
+        "ds_read_b64_tr_b16 %4, %16 offset:2048\n"
+        "ds_read_b64_tr_b16 %5, %16 offset:3072\n"
+        "ds_read_b64_tr_b16 %6, %17 offset:2048\n"
+        "ds_read_b64_tr_b16 %7, %17 offset:3072\n"
+        "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+        "ds_read_b64_tr_b16 %9, %16 offset:5120\n"
+        "ds_read_b64_tr_b16 %10, %17 offset:4096\n"
+        "ds_read_b64_tr_b16 %11, %17 offset:5120\n"
+        "ds_read_b64_tr_b16 %12, %16 offset:6144\n"
+        "ds_read_b64_tr_b16 %13, %16 offset:7168\n"
+        "ds_read_b64_tr_b16 %14, %17 offset:6144\n"
+        "ds_read_b64_tr_b16 %15, %17 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+        : "v"(base[0]), "v"(base[1]), "v"(busy[0]), "v"(busy[1]), "v"(busy[2]), "v"(busy[3])
+        : "memory");
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) vf[kk][n] = join_bf16x4(x[4 * kk + 2 * n], x[4 * kk + 2 * n + 1]);
 }
 
 // Partials combined per round trip by the last chunk of a cut tile.
@@ -364,6 +398,9 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   // numerator uses); only element 0 is read and rescaled.  At d = 128 the
   // matrix core is the busier one and the sums stay on the vector ALUs.
   constexpr bool kSumOnMfma = D == 64;
+  // d = 64 without the vote: all of a block's V fragments fit beside the
+  // scores, so they are read once, under the QK^T products
+  constexpr bool kVAll = D == 64 && !DYN;
   f32x16 lacc = f32x16{};
   float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // vector-ALU form: this lane's half, four partial sums
   bf16x8 ones;
@@ -432,6 +469,10 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 
     // ---- S^T = K Q^T : two 32-key tiles; K-fragment reads run four MFMAs ahead
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    uint32_t vb[NTD];
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
+    bf16x8 vall[4][2];
     {
       constexpr int NS = 2 * KS;
       auto kread = [&](int st) __attribute__((always_inline)) {
@@ -446,6 +487,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         if (st + 4 < NS) kfr[st & 3] = kread(st + 4);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the block's V fragments, under these products.  Products that may not
+      // have started when the loads land are the last QK^T ones (each product
+      // starts only after the one issued before it, and the previous block's
+      // P.V products came before all of these): their K fragments are busy
+      // inputs, Q and the scores stay live.
+      if constexpr (kVAll) read_v_all64(vall, vb, kfr);
     }
 
     // ---- masks: causal diagonal, invalid keys, rows past Nq
@@ -543,35 +590,41 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         }
       }
       // ---- O^T += V^T P^T : 4 key steps of 16 x NTD d tiles
-      uint32_t vb[NTD];
+      if constexpr (kVAll) {
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
-      // two fragment sets in turn: a step's loads never land on the operands
-      // of the previous step's products.  Before the first step no product is
-      // in flight: the block row max waited for the last QK^T product, and the
-      // matrix pipe runs a wave's products in order.
-      bf16x8 va[NTD], vb2[NTD];
-      if constexpr (NTD == 4) {
-        read_v_step<D, 0>(va, vb, pf, pf[3]);  // (the P fragments: live anyway, nothing to protect)
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+          for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vall[kk][n], pf[kk], oacc[n]);
+          lacc = mfma32(ones, pf[kk], lacc);
+        }
       } else {
-        const bf16x8 live[NTD] = {pf[2], pf[3]};
-        read_v_step<D, 0>(va, vb, live, pf[1]);
+        // two fragment sets in turn: a step's loads never land on the operands
+        // of the previous step's products.  Before the first step no product is
+        // in flight: the block row max waited for the last QK^T product, and the
+        // matrix pipe runs a wave's products in order.
+        bf16x8 va[NTD], vb2[NTD];
+        if constexpr (NTD == 4) {
+          read_v_step<D, 0>(va, vb, pf, pf[3]);  // (the P fragments: live anyway, nothing to protect)
+        } else {
+          const bf16x8 live[NTD] = {pf[2], pf[3]};
+          read_v_step<D, 0>(va, vb, live, pf[1]);
+        }
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[0], oacc[n]);
+        if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[0], lacc);
+        read_v_step<D, 1>(vb2, vb, va, pf[0]);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[1], oacc[n]);
+        if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[1], lacc);
+        read_v_step<D, 2>(va, vb, vb2, pf[1]);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[2], oacc[n]);
+        if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[2], lacc);
+        read_v_step<D, 3>(vb2, vb, va, pf[2]);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[3], oacc[n]);
+        if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[3], lacc);
       }
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[0], oacc[n]);
-      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[0], lacc);
-      read_v_step<D, 1>(vb2, vb, va, pf[0]);
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[1], oacc[n]);
-      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[1], lacc);
-      read_v_step<D, 2>(va, vb, vb2, pf[1]);
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(va[n], pf[2], oacc[n]);
-      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[2], lacc);
-      read_v_step<D, 3>(vb2, vb, va, pf[2]);
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) oacc[n] = mfma32(vb2[n], pf[3], oacc[n]);
-      if constexpr (kSumOnMfma) lacc = mfma32(ones, pf[3], lacc);
     } else {
       ++skipped;
     }
