@@ -14,9 +14,9 @@
 //   if kept:     P = 2^(S*scale*log2e - m),  l += rowsum(P),
 //                O^T += V^T P^T  (V read transposed from LDS with
 //                ds_read_b64_tr_b16: at d = 128 one key step at a time,
-//                each step's reads under the previous step's products; at
-//                d = 64 without the vote, all four steps at once under the
-//                QK^T products)
+//                the first under the QK^T products, each later one under
+//                the previous step's products; at d = 64 without the vote,
+//                all four steps at once under the QK^T products)
 //
 // Layout choice: computing S^T (keys x rows) puts one query row per lane
 // (row = lane % 32, split over lanes l and l+32), so the row max, the row
@@ -473,6 +473,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
 #pragma unroll
     for (int n = 0; n < NTD; ++n) vb[n] = lds_addr(vtile + Tile<D>::vpos(vr0, 4 * n + vcs) + vhalf);
     bf16x8 vall[4][2];
+    bf16x8 va[NTD];
     {
       constexpr int NS = 2 * KS;
       auto kread = [&](int st) __attribute__((always_inline)) {
@@ -493,6 +494,8 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       // P.V products came before all of these): their K fragments are busy
       // inputs, Q and the scores stay live.
       if constexpr (kVAll) read_v_all64(vall, vb, kfr);
+      // d = 128: the first key step's V fragments (same rule)
+      if constexpr (D == 128 && !MAXONLY) read_v_step<D, 0>(va, vb, kfr, kfr[3]);
     }
 
     // ---- masks: causal diagonal, invalid keys, rows past Nq
@@ -599,13 +602,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         }
       } else {
         // two fragment sets in turn: a step's loads never land on the operands
-        // of the previous step's products.  Before the first step no product is
-        // in flight: the block row max waited for the last QK^T product, and the
-        // matrix pipe runs a wave's products in order.
-        bf16x8 va[NTD], vb2[NTD];
-        if constexpr (NTD == 4) {
-          read_v_step<D, 0>(va, vb, pf, pf[3]);  // (the P fragments: live anyway, nothing to protect)
-        } else {
+        // of the previous step's products.  At d = 128 the first step's set
+        // was read under the QK^T products; at d = 64 it is read here, when no
+        // product is in flight (the block row max waited for the last QK^T
+        // product, and the matrix pipe runs a wave's products in order).
+        bf16x8 vb2[NTD];
+        if constexpr (D == 64) {
           const bf16x8 live[NTD] = {pf[2], pf[3]};
           read_v_step<D, 0>(va, vb, live, pf[1]);
         }
