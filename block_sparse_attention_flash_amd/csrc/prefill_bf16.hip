@@ -488,11 +488,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         if (st + 4 < NS) kfr[st & 3] = kread(st + 4);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the block's V fragments, under these products.  Products that may not
-      // have started when the loads land are the last QK^T ones (each product
-      // starts only after the one issued before it, and the previous block's
-      // P.V products came before all of these): their K fragments are busy
-      // inputs, Q and the scores stay live.
+      // the block's V fragments, under these products.  A wave issues a
+      // product only when the matrix pipe takes it, so the products that may
+      // not yet have read their operands when these loads land are the last
+      // few QK^T ones (the previous block's P.V products were issued before
+      // all of them): the K fragments of the last four are busy inputs, Q and
+      // the scores stay live.
       if constexpr (kVAll) read_v_all64(vall, vb, kfr);
       // d = 128: the first key step's V fragments (same rule)
       if constexpr (D == 128 && !MAXONLY) read_v_step<D, 0>(va, vb, kfr, kfr[3]);
