@@ -624,8 +624,9 @@ def main(argv=None) -> int:
                     help="first run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the kernels need no collectives; "
-                                   "see DESIGN.md for how the path would shard across GPUs", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "runs on one GPU only: the kernels need no collectives; the path would "
+                                   "shard by (batch, head) or by query tiles, one process per GPU",
+                          "n_gpus": a.gpus}))
         return 2
     import torch
     if not torch.cuda.is_available():
