@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   BSATTN_OK = 0,
   BSATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, lambda out of range, malformed CSR */
-  BSATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (dtype, d, tile) */
+  BSATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (dtype, d, tile) */
   BSATTN_ERR_CAPACITY = 3,    /* caller buffer too small (col_idx capacity, workspace) */
   BSATTN_ERR_HIP = 4          /* a HIP call or kernel launch failed */
 } bsattn_status;
