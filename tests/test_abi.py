@@ -173,9 +173,9 @@ def test_decode_rejects(name, mutate, status):
 
 
 def test_decode_split_policy():
-    # automatic: splits of at most 64 blocks, enough work-groups for the chip
+    # automatic: splits of at most 56 blocks (7/8 of the 64-block cap), enough work-groups for the chip
     S = bsa.decode_num_splits(32, 32, 8, 131072, 128)
-    assert S == 32
+    assert S == 37                                                    # ceil(2048 / 56)
     assert bsa.decode_num_splits(1, 32, 8, 131072, 128) == 256      # 8 blocks per split: 2048 work-groups
     assert bsa.decode_num_splits(1, 4, 1, 4096, 128) >= 2
     # an explicit count is honoured up to 64 blocks per split (one 64-bit skip mask)
@@ -183,7 +183,7 @@ def test_decode_split_policy():
     assert bsa.decode_num_splits(1, 4, 1, 64 * 64, 128, num_splits=1) == 1
     assert bsa.decode_num_splits(1, 4, 1, 128 * 64, 128, num_splits=1) == 2
     # blocks per split: S = ceil(Tc / n)
-    assert bsa.decode_split_blocks(32, 32, 8, 131072, 128) == 64
+    assert bsa.decode_split_blocks(32, 32, 8, 131072, 128) == 56
     assert bsa.decode_split_blocks(1, 4, 1, 64 * 10, 128, num_splits=3) == 4
     assert bsa.decode_split_blocks(1, 4, 1, 128 * 64, 128, num_splits=1) == 64
     assert bsa.decode_split_blocks(1, 4, 3, 64, 128) == 0                        # Hq % Hkv != 0
