@@ -232,8 +232,8 @@ def prefill_workspace_size(B: int, Hq: int, d: int, n_slots: int) -> int:
 
 
 def prefill_workspace(B: int, Hq: int, d: int, n_slots: int, device):
-    """A zero-filled prefill workspace (its arrival counters must start at zero;
-    each call leaves them at zero, so the tensor can be reused on one stream)."""
+    """A prefill workspace (zero-filled; every call zeroes the words it counts
+    with, so calls of any shape can reuse it on one stream)."""
     return _torch().zeros(prefill_workspace_size(B, Hq, d, n_slots), dtype=_torch().uint8, device=device)
 
 
@@ -436,8 +436,9 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 6
 
 
 def decode_workspace(B: int, Hq: int, Hkv: int, L: int, d: int, device, Bc: int = 64, num_splits: int = 0):
-    """A zero-filled decode workspace (tickets, flags and counters must start at
-    zero; each call leaves them at zero, so the tensor can be reused on one stream)."""
+    """A zero-filled decode workspace (the header's health word must start at
+    zero; every call zeroes its tickets and flags, so calls of any shape can
+    reuse it on one stream)."""
     torch = _torch()
     return torch.zeros(decode_workspace_size(B, Hq, Hkv, L, d, Bc, num_splits), dtype=torch.uint8, device=device)
 

@@ -72,7 +72,7 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   size_t off = 0;
   w.o = off;   off = align256(off + units * 128 * (size_t)d * sizeof(float));
   w.ml = off;  off = align256(off + units * 128 * 2 * sizeof(float));
-  w.cnt = off; off = align256(off + units * 2 * sizeof(int32_t));
+  w.cnt = off; off = align256(off + units * 4 * sizeof(int32_t));  // {visited, skipped, rows agreeing, -}
   w.arrive = off; off = align256(off + units * sizeof(int32_t));  // n_merges <= n_slots
   w.pre = off; off = align256(off + units * 128 * kPreSplit * sizeof(float));
   w.total = off;

@@ -28,9 +28,15 @@
 //            scores stay out of LDS: the work-group stays small, so enough of
 //            them share a CU to keep HBM busy while some sit in phases 2-3.
 //   combine  merge the splits of each (sequence, head): online-softmax
-//            rescaling (attention tutorial section 4.2); it also clears the
-//            pair's ticket and look-back flags, so the workspace needs no
-//            clearing between calls (only a zero fill before its first use)
+//            rescaling (attention tutorial section 4.2)
+//
+// The tickets and look-back flags of a call are cleared by a small kernel
+// launched just before the split kernel, on the same stream.  Their offsets
+// depend on the call's shape (the split count S), so a workspace reused with
+// another shape may hold any bytes there (an earlier call's partials); the
+// clear makes every word the split kernel waits on or counts with start at
+// zero whatever the workspace held.  Only the health word in the fixed
+// header must be zero before the first call.
 //
 // Forward progress: a work-group takes its (sequence, K/V head) from its index
 // and its split number from an atomic ticket of that pair, so a split only
@@ -125,6 +131,13 @@ __device__ __forceinline__ void block_scores(f32x4 (&acc)[4], const bf16x8 (&kf)
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Zero the tickets [B*Hkv] and look-back flags [B*Hkv*S] of this call.
+__global__ __launch_bounds__(NT) void decode_clear_kernel(int* tickets, int n_tickets, int* flags, int n_flags) {
+  const int stride = gridDim.x * NT;
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n_tickets; i += stride) tickets[i] = 0;
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n_flags; i += stride) flags[i] = 0;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, DecodeWorkspace wl) {
   __shared__ DecSmem<D, G> sm;
@@ -149,6 +162,10 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(const DecodeParams p, 
   if (tid == 0) sm.ticket = atomicAdd(&tickets[pair], 1);
   __syncthreads();
   const int s = sm.ticket;
+  if (s < 0 || s >= S) {  // cannot happen after the clear kernel; never index past the workspace
+    if (tid == 0) atomicOr(&header[1], 2);
+    return;
+  }
   const int b = pair / p.Hkv, g = pair % p.Hkv;
   const int unit = pair * S + s;
   // split s in visiting order: ascending, its blocks are [s bps, (s+1) bps);
@@ -563,8 +580,12 @@ __global__ __launch_bounds__(NT) void decode_dense_kernel(const DecodeParams p, 
     stats[((int64_t)unit * G + tid) * 2 + 1] = l;
   }
   if (tid == 0) counts[unit] = 0;
-  if (p.block_state)
+  if (p.block_state && p.per_head) {  // [B, Hq, Tc]: every head of the group computes every block
+    for (int x = tid; x < G * nb; x += NT)
+      p.block_state[((int64_t)b * p.Hq + g * G + x / nb) * p.Tc + blk0 + x % nb] = 1;
+  } else if (p.block_state) {
     for (int lb = tid; lb < nb; lb += NT) p.block_state[((int64_t)b * p.Hkv + g) * p.Tc + blk0 + lb] = 1;
+  }
 }
 
 // Merge the S split partials of one (sequence, query head); write bf16 output
@@ -626,21 +647,22 @@ __global__ __launch_bounds__(NT) void decode_combine_kernel(const DecodeParams p
     p.counters[2 * pair + 0] = p.Tc;
     p.counters[2 * pair + 1] = sk;
   }
-  if (r == 0) {  // every split of the pair has finished: clear its ticket and flags
-    int* tickets = reinterpret_cast<int*>(ws + wl.tickets);
-    int* flags = reinterpret_cast<int*>(ws + wl.flags);
-    for (int s = tid; s < S; s += NT) flags[pair * S + s] = 0;
-    if (tid == 0) tickets[pair] = 0;
-  }
 }
 
 template <int D, int G>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const DecodeWorkspace wl = decode_workspace_layout(p.B, p.Hq, p.Hkv, p.d, p.num_splits);
   const int units = p.B * p.Hkv * p.num_splits;
-  if (p.lambda > 0.0f)
+  if (p.lambda > 0.0f) {
+    char* ws = static_cast<char*>(p.workspace);
+    const int n_tickets = p.B * p.Hkv;
+    const int clear_grid = min(64, (units + NT - 1) / NT);
+    hipLaunchKernelGGL(decode_clear_kernel, dim3(clear_grid), dim3(NT), 0, s, reinterpret_cast<int*>(ws + wl.tickets),
+                       n_tickets, reinterpret_cast<int*>(ws + wl.flags), units);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
-  else
+  } else
     hipLaunchKernelGGL((decode_dense_kernel<D, G>), dim3(units), dim3(NT), 0, s, p, wl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

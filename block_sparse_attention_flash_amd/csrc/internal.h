@@ -47,7 +47,7 @@ struct PrefillParams {
   int32_t n_slots;
   float* part_o;                // [n_slots][B][Hq][128 * d], in accumulator order (see the kernel)
   float* part_ml;               // [n_slots][B][Hq][128][2]  (reference max in raw score units, row sum)
-  int32_t* part_cnt;            // [n_slots][B][Hq][2]
+  int32_t* part_cnt;            // [n_slots][B][Hq][4] {visited, skipped, rows agreeing, unused}
   int32_t* arrive;              // [n_merges][B][Hq] chunk arrival counters (zero between calls)
   float* part_pre;              // [n_slots][B][Hq][kPreSplit][128] lambda > 0: per-row max of each share of a chunk
   int32_t rank_major;           // bf16 kernel: XCD work order (set by its launcher)

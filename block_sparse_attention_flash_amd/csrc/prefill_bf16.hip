@@ -326,9 +326,12 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
   slot = __builtin_amdgcn_readfirstlane(slot);
   mrg = __builtin_amdgcn_readfirstlane(mrg);
   if constexpr (MAXONLY) {
+    const int s0 = p.sched_merges[3 * mrg + 1], ns = p.sched_merges[3 * mrg + 2];
+    // this launch runs before the main one: it zeroes the merge's arrival
+    // counter (the workspace may hold anything there, see the launcher)
+    if (slot == s0 && sub == 0 && tid == 0) p.arrive[((int64_t)mrg * p.B + b) * p.Hq + h] = 0;
     // the chunk visited last (ascending: the highest slot; descending: the
     // lowest) has no later chunk that reads its maxima
-    const int s0 = p.sched_merges[3 * mrg + 1], ns = p.sched_merges[3 * mrg + 2];
     if (slot == (p.block_order ? s0 : s0 + ns - 1)) return;
   }
 
@@ -648,6 +651,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     l_tot = l_part + __shfl_xor(l_part, 32);
   }
   int vis_tot = nblk, skip_tot = skipped;
+  int rows_tot = 0;  // row_counters: the work item's four waves (LDS words; the vote words are free now)
+  if (p.row_counters) {
+    __syncthreads();
+    if (lane == 0) sm.vote[1][wave] = rows_agree;
+    __syncthreads();
+    rows_tot = sm.vote[1][0] + sm.vote[1][1] + sm.vote[1][2] + sm.vote[1][3];
+  }
 
   if (slot >= 0) {
     // ---- chunk of a cut tile: publish the partial (unnormalised O relative
@@ -671,8 +681,9 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         store_coherent(p.part_ml + (unit(slot) * BR + lrow) * 2 + 1, l_tot);
       }
       if (tid == 0) {
-        store_coherent(p.part_cnt + unit(slot) * 2 + 0, nblk);
-        store_coherent(p.part_cnt + unit(slot) * 2 + 1, skipped);
+        store_coherent(p.part_cnt + unit(slot) * 4 + 0, nblk);
+        store_coherent(p.part_cnt + unit(slot) * 4 + 1, skipped);
+        store_coherent(p.part_cnt + unit(slot) * 4 + 2, rows_tot);
       }
     }
     wait_stores_done();
@@ -722,11 +733,14 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     }
     l_tot = l;
     m_ref = M;
-    if (p.tile_counters && tid == 0) {
+    if ((p.tile_counters || p.row_counters) && tid == 0) {
       vis_tot = skip_tot = 0;
+      int rows_own = rows_tot;
+      rows_tot = 0;
       for (int sl = s0; sl < s0 + ns; ++sl) {
-        vis_tot += sl == slot ? nblk : load_coherent(p.part_cnt + unit(sl) * 2);
-        skip_tot += sl == slot ? skipped : load_coherent(p.part_cnt + unit(sl) * 2 + 1);
+        vis_tot += sl == slot ? nblk : load_coherent(p.part_cnt + unit(sl) * 4);
+        skip_tot += sl == slot ? skipped : load_coherent(p.part_cnt + unit(sl) * 4 + 1);
+        rows_tot += sl == slot ? rows_own : load_coherent(p.part_cnt + unit(sl) * 4 + 2);
       }
     }
   }
@@ -754,14 +768,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     tc[0] = vis_tot;
     tc[1] = skip_tot;
   }
-  if (p.row_counters) {  // the tile's four waves: one LDS word each (the vote words are free now)
-    __syncthreads();
-    if (lane == 0) sm.vote[0][wave] = rows_agree;
-    __syncthreads();
-    if (tid == 0)
-      p.row_counters[((int64_t)b * p.Hq + h) * p.Tr + t] = sm.vote[0][0] + sm.vote[0][1] + sm.vote[0][2] + sm.vote[0][3];
-  }
+  if (p.row_counters && tid == 0) p.row_counters[((int64_t)b * p.Hq + h) * p.Tr + t] = rows_tot;
 #endif
+}
+
+// Zero n words (the arrival counters of a call whose schedule cuts tiles).
+__global__ __launch_bounds__(NT) void clear_words_kernel(int32_t* w, int n) {
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) w[i] = 0;
 }
 
 template <int D, bool CAUSAL, bool DYN>
@@ -771,9 +784,19 @@ hipError_t launch(const PrefillParams& p0, hipStream_t s) {
   const int64_t grid = (int64_t)p.B * p.Hq * units;
   // rank-major when one XCD (32 CUs) has under four waves of work-groups
   p.rank_major = grid / 8 < 4 * 32 * kMinBlocksPerCu<D> ? 1 : 0;
-  if (DYN && p.n_slots > 0) {  // cut tiles: the chunk maxima first, kPreSplit work-groups per chunk and head
+  // Cut tiles: the arrival counters sit at offsets that depend on the call's
+  // shape (n_slots), so a workspace reused with another shape may hold any
+  // bytes there.  A launch before the main one zeroes them: the chunk-maximum
+  // pass when lambda > 0 (kPreSplit work-groups per chunk and head), else a
+  // small clear kernel.
+  if (DYN && p.n_slots > 0) {
     const int64_t pre_grid = (int64_t)p.n_slots * p.B * p.Hq * kPreSplit;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true, true>), dim3((unsigned)pre_grid), dim3(NT), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (p.n_slots > 0) {
+    const int n = p.n_merges * p.B * p.Hq;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)min(64, (n + NT - 1) / NT)), dim3(NT), 0, s, p.arrive, n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -229,10 +229,13 @@ typedef struct {
   int32_t n_slots;             /* partial slots of the schedule (cut tiles) */
   void* workspace;             /* device, >= bsattn_prefill_workspace_size(B, Hq, d, n_slots) bytes,
                                   256-byte aligned; unused when n_slots == 0.  Holds the
-                                  partials and one arrival counter per (merge, batch, head):
-                                  zero-fill it once before its first use; every call leaves
-                                  the counters at zero again.  Calls that share a workspace
-                                  must not overlap (same stream, or ordered by events). */
+                                  partials and one arrival counter per (merge, batch, head).
+                                  No initial contents are needed, and calls of any shape may
+                                  share it: a launch ahead of the main kernel zeroes the
+                                  call's arrival counters (the chunk-maximum pass when
+                                  lambda > 0, else a small clear kernel).  Calls that share a
+                                  workspace must not overlap (same stream, or ordered by
+                                  events). */
   size_t workspace_bytes;
   float* lse;             /* optional device [B, Hq, Nq] float32: each row's natural-log sum of
                              exp(scale q.k) over the keys it attended (-inf for a row with none),
@@ -347,8 +350,12 @@ typedef struct {
                              beyond float rounding order; never changes the skip set (except under
                              max_scope = 1, below) */
   void* workspace;        /* device, >= bsattn_decode_workspace_size(...) bytes, 256-byte aligned.
-                             Tickets, flags and counters: zero-fill it once before its first use;
-                             every call leaves them at zero again.  Calls that share a workspace
+                             Its first 256 bytes are a header holding the health word (read by
+                             bsattn_decode_check): zero them once before the first use (a zero
+                             fill of the whole buffer does).  The rest needs no initial contents,
+                             and calls of any shape may share the workspace: with lambda > 0 a
+                             small kernel launched ahead of the split kernel zeroes the call's
+                             split tickets and look-back flags.  Calls that share a workspace
                              must not overlap (same stream, or ordered by events). */
   size_t workspace_bytes;
   int32_t* counters;      /* optional device [B, Hkv, 2] int32: {visited, skipped} blocks, where a
@@ -381,8 +388,10 @@ int32_t bsattn_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, 
 int32_t bsattn_decode_split_blocks(int32_t B, int32_t Hq, int32_t Hkv, int32_t L, int32_t d,
                                    int32_t Bc, int32_t num_splits);
 
-/* Enqueue the decode on `stream`: the split kernel, then the combine kernel
- * (merge of the splits, attention tutorial section 4.2). */
+/* Enqueue the decode on `stream`: with lambda > 0 the clear of the call's
+ * tickets and flags, the split kernel (BLASST skipping with the exact running
+ * max), then the combine kernel (merge of the splits, attention tutorial
+ * section 4.2); with lambda = 0 a single-pass split kernel and the combine. */
 bsattn_status bsattn_decode_fwd(const bsattn_decode_args* args, void* stream);
 
 /* Read and clear the decode workspace health word after the stream has

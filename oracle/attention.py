@@ -213,6 +213,41 @@ def skip_set_vectorized(qr, k, rows, blocks, Bc: int, scale: float, lam: float,
     return skip, bm
 
 
+def skip_set_batched(qr, k, rows, blocks, Bc: int, scale: float, lam: float,
+                     n_valid: int, causal: bool):
+    """The closed form of ``skip_set_vectorized`` with the scores of all the
+    tile's visited blocks taken in one float64 product (torch CPU), for
+    full-size checks: the block maxima are the row maxima of each block's
+    allowed scores, the running max their cumulative maximum in visiting
+    order, and a block is skipped iff every row has no allowed key in it or
+    a gap below ln(lambda) (BLASST notes, Algorithm 1 and section 4).
+    Returns (skip [nb], margin [nb]) with margin as in ``blasst_tile``."""
+    import torch
+    lnl = log_threshold(lam)
+    n_k = k.shape[0]
+    nb = len(blocks)
+    if nb == 0:
+        return np.zeros(0, bool), np.zeros(0)
+    blocks = np.asarray(blocks, dtype=np.int64)
+    keys = (blocks[:, None] * Bc + np.arange(Bc)[None, :]).reshape(-1)     # [nb * Bc], padded blocks
+    inside = keys < n_k
+    kk = torch.as_tensor(k, dtype=torch.float64) if not isinstance(k, torch.Tensor) else k.to(torch.float64)
+    qq = torch.as_tensor(qr, dtype=torch.float64) if not isinstance(qr, torch.Tensor) else qr.to(torch.float64)
+    S = scale * (qq @ kk[torch.from_numpy(np.where(inside, keys, 0))].T)  # [R, nb * Bc]
+    allowed = torch.from_numpy(inside & (keys < n_valid))[None, :].expand(len(rows), -1)
+    if causal:
+        allowed = allowed & (torch.from_numpy(keys)[None, :] <= torch.from_numpy(np.asarray(rows))[:, None])
+    S = torch.where(allowed, S, torch.tensor(-math.inf, dtype=torch.float64))
+    bm = S.view(len(rows), nb, Bc).amax(dim=2)                          # [R, nb]
+    cm = torch.cummax(bm, dim=1).values
+    finite = torch.isfinite(bm)
+    gap = torch.where(finite, bm - torch.where(torch.isfinite(cm), cm, torch.zeros_like(cm)),
+                      torch.tensor(-math.inf, dtype=torch.float64))
+    skip = torch.all(~finite | (gap < lnl), dim=0).numpy() if lam > 0.0 else np.zeros(nb, bool)
+    margin = (gap.amax(dim=0) - lnl).numpy() if lam > 0.0 else np.full(nb, np.inf)
+    return skip, margin
+
+
 def row_agreement(qr, k, rows, blocks, Bc: int, scale: float, lam: float, n_valid: int, causal: bool):
     """Per-row form of the BLASST skip condition, for the per-row against
     tile-wide comparison: walk the visited blocks as Algorithm 1 does (running

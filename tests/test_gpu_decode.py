@@ -240,7 +240,8 @@ def test_decode_variants(max_scope, decisions, order, num_splits, G, d):
     qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
     bps = bsa.decode_split_blocks(cfg.B, cfg.Hq, Hkv, L, d, 64, num_splits) if max_scope == "split" else 0
     tot = [0, 0, 0]
-    for lam in (cfg.lam, 0.05, 0.4):
+    lams = (cfg.lam, 0.05, 0.4) + ((0.0,) if decisions == "head" else ())   # lambda 0: the single-pass kernel
+    for lam in lams:
         out, st, cnt = run_decode(cfg, qd, kd, vd, num_splits=num_splits, lam=lam, order=order,
                                   max_scope=max_scope, decisions=decisions)
         for b in range(cfg.B):
@@ -248,3 +249,35 @@ def test_decode_variants(max_scope, decisions, order, num_splits, G, d):
             tot = [x + y for x, y in zip(tot, r)]
     _say(f"  decisions {tot[0]}, skipped {tot[1]}, V blocks not loaded {tot[2]}")
     assert tot[1] > 0
+
+
+def test_decode_workspace_any_contents():
+    """One workspace, filled with random bytes (header zeroed) and reused by
+    calls whose split count, batch and head count grow and shrink: each call
+    zeroes the tickets and flags it uses, so stale words of an earlier shape
+    (partials now lying where this call's flags are) never count."""
+    _say("decode workspace with arbitrary contents, shapes changing between calls")
+    cases = [  # (B, Hq, Hkv, L, d, num_splits)
+        (2, 8, 2, 3000, 128, 3), (2, 8, 2, 3000, 128, 7), (3, 16, 4, 2500, 64, 47), (2, 8, 2, 3000, 128, 0),
+        (1, 4, 1, 6000, 128, 9), (3, 16, 4, 2500, 64, 2)]
+    need = max(bsa.decode_workspace_size(B, Hq, Hkv, L, d, 64, S) for B, Hq, Hkv, L, d, S in cases)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=g)
+    ws[:256] = 0
+    for i, (B, Hq, Hkv, L, d, S) in enumerate(cases):
+        cfg = DecodeWorkload(name="ws", description="", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, Bc=64, lam=40.0 / L,
+                             seed=40 + i)
+        _say(f"  B{B} Hq{Hq} Hkv{Hkv} L{L} d{d} splits {S} "
+             f"({bsa.decode_num_splits(B, Hq, Hkv, L, d, 64, S)} per pair)")
+        q, kc, vc = gen_decode_inputs(cfg)
+        Tc = -(-L // 64)
+        state = torch.zeros((B, Hkv, Tc), dtype=torch.uint8, device=DEV)
+        counters = torch.full((B, Hkv, 2), -1, dtype=torch.int32, device=DEV)
+        out = bsa.decode_fwd(q.to(DEV), kc.to(DEV), vc.to(DEV), L=L, scale=cfg.scale, lam=cfg.lam, num_splits=S,
+                             workspace=ws, counters=counters, block_state=state)
+        torch.cuda.synchronize()
+        assert bsa.decode_check(ws) == 0, "decode look-back wait timed out or a ticket was out of range"
+        out, st, cnt = out.cpu(), state.cpu().numpy(), counters.cpu().numpy()
+        for b in range(B):
+            check_sequence(q[b], kc[b], vc[b], out, st, cnt, b, L, cfg.scale, cfg.lam)

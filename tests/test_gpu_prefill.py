@@ -425,3 +425,87 @@ def test_descending_block_order(dtype, d):
                                            col_idx=None if csr is None else csr[1], order="descending")
                     tot = [x + y for x, y in zip(tot, r)]
         _say(f"  visited {tot[0]} skipped {tot[1]} excused {tot[2]}")
+
+
+def test_prefill_workspace_any_contents():
+    """One prefill workspace, filled with random bytes, reused by cut-tile
+    schedules whose slot count grows and shrinks, with and without BLASST:
+    each call zeroes its arrival counters before the main launch, so stale
+    words of an earlier layout never count as arrivals."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    cases = [(3, 0.0, 2), (1, 0.0, 2), (9, 0.3, 1), (1, 0.3, 2), (2, 0.0, 1), (1, 0.0, 2)]  # (max_blocks, lam, B)
+    scheds = [bsa.build_schedule(csr[0], mb) for mb, _, _ in cases]
+    need = max(bsa.prefill_workspace_size(B, 4, 128, max(sc.n_slots, 1)) for sc, (_, _, B) in zip(scheds, cases))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(98)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=g)
+    for (mb, lam, B), sched in zip(cases, scheds):
+        cfg = _small("ws", N=n, d=128, B=B, Hq=4, Hkv=2, mask=spec, generator="sink", causal=False, lam=lam)
+        _say(f"prefill workspace with arbitrary contents: max_blocks {mb} ({sched.n_slots} slots) lambda {lam} B{B}")
+        q, k, v = gen_prefill_inputs(cfg)
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, schedule=sched, workspace=ws)
+        for b in range(B):
+            for h in range(cfg.Hq):
+                for t in range(-(-n // 128)):
+                    check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=128, Bc=64, scale=cfg.scale,
+                                       causal=False, lam=lam, n_valid=n, row_ptr=csr[0], col_idx=csr[1])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_counters_cut_tiles(d):
+    """Per-row skip conditions with a schedule that cuts tiles into chunks:
+    every chunk publishes its count and the merging chunk sums them."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    for lam, order in ((0.3, "ascending"), (0.6, "descending")):
+        cfg = _small("rows_cut", N=n, d=d, Hq=4, Hkv=2, lam=lam, mask=spec,
+                     generator="sink" if order == "ascending" else "sink_last", seed=13)
+        _say(f"row counters with cut tiles d{d} lambda {lam} {order}")
+        q, k, v = gen_prefill_inputs(cfg)
+        sched = bsa.build_schedule(csr[0], 2)
+        assert sched.n_merges > 0
+        Tr = -(-n // 128)
+        rc = torch.full((cfg.B, cfg.Hq, Tr), -1, dtype=torch.int32, device=DEV)
+        bsa.prefill_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=cfg.scale, lam=lam, row_ptr=torch.from_numpy(csr[0]).to(DEV),
+                        col_idx=torch.from_numpy(csr[1]).to(DEV), n_valid=n, row_counters=rc, schedule=sched,
+                        order=order)
+        torch.cuda.synchronize()
+        rc = rc.cpu().numpy()
+        total = 0
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                g = A.kv_head_of(h, cfg.Hq, cfg.Hkv)
+                for t in range(Tr):
+                    rows = A.tile_rows(t, 128, n)
+                    blocks = A.visited_blocks(t, 128, 64, n, n, False, *csr, order=order)
+                    agree, gaps = A.row_agreement(A.as_f64(q[b, rows[0]:rows[-1] + 1, h]), k[b, :, g], rows, blocks,
+                                                  64, cfg.scale, lam, n, False)
+                    near = int(np.count_nonzero(np.abs(gaps - np.log(lam)) <= 1e-3))
+                    assert abs(int(rc[b, h, t]) - int(agree.sum())) <= near, (b, h, t, rc[b, h, t], agree.sum())
+                    total += int(agree.sum())
+        assert total > 0
+
+
+@pytest.mark.parametrize("d,Br", [(64, 128), (128, 64), (128, 128)])
+def test_fp32_instances(d, Br):
+    """The fp32 vector path at every head dim and tile height it accepts:
+    static CSR, causal with BLASST, dense with a ragged tail; 1e-5 max-abs."""
+    spec = video_text_spec(frames=3, grid=8, text=20, radius=1, t_radius=1, anchors=4, unit=8)
+    n = spec.n_valid
+    for causal, lam, csr_on, gen in ((False, 0.0, True, "iid"), (True, 0.3, True, "sink"), (True, 0.0, False, "iid"),
+                                     (False, 0.5, False, "sink")):
+        cfg = _small("f32i", dtype="fp32", N=n, d=d, Hq=4, Hkv=2, causal=causal, lam=lam, mask=spec, generator=gen,
+                     Br=Br, seed=15)
+        _say(f"fp32 d{d} Br{Br} causal={causal} lambda {lam} csr={csr_on}")
+        q, k, v = gen_prefill_inputs(cfg)
+        csr = bsa.build_block_index(spec, n, n, Br, 64) if csr_on else None
+        out, st, cnt = run_prefill(cfg, q.to(DEV), k.to(DEV), v.to(DEV), csr=csr, Br=Br)
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                for t in range(-(-n // Br)):
+                    check_prefill_tile(q, k, v, out, st, cnt, b, h, t, Br=Br, Bc=64, scale=cfg.scale, causal=causal,
+                                       lam=lam, n_valid=n, row_ptr=None if csr is None else csr[0],
+                                       col_idx=None if csr is None else csr[1], fp32=True)

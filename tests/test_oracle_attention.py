@@ -444,3 +444,42 @@ def test_lambda_range_rejected():
     for bad in (-0.1, 1.0, 2.0):
         with pytest.raises(ValueError):
             A.log_threshold(bad)
+
+
+# ---- the batched closed form equals the per-block loop and Algorithm 1 ------
+
+@pytest.mark.parametrize("causal,n_valid,order", [(False, 300, "ascending"), (True, 300, "ascending"),
+                                                  (False, 270, "descending"), (True, 300, "descending")])
+def test_skip_set_batched_equals_loop(causal, n_valid, order):
+    """skip_set_batched (one product per tile, torch float64) takes the same
+    decisions as skip_set_vectorized and the literal Algorithm 1 loop, and its
+    margins equal blasst_tile's, on a ragged last block, padding keys, causal
+    diagonal tiles, a CSR list and both visiting orders."""
+    n, d, Br, Bc = 300, 32, 128, 64
+    g = np.random.default_rng(77)
+    q = g.standard_normal((n, d))
+    k = g.standard_normal((n, d))
+    v = g.standard_normal((n, d))
+    w = g.standard_normal(d)
+    w /= np.linalg.norm(w)
+    q += 4.0 * w                                      # a sink: later blocks fall below the threshold
+    k[:64] += 12.0 * w
+    row_ptr = np.array([0, 3, 4, 9])
+    col_idx = np.array([0, 2, 4, 1, 0, 1, 2, 3, 4])
+    n_skipped = 0
+    for lam in (0.05, 0.3, 0.0):
+        for t in range(3):
+            for csr in (False, True):
+                rows = A.tile_rows(t, Br, n)
+                blocks = A.visited_blocks(t, Br, Bc, n, n, causal, *((row_ptr, col_idx) if csr else (None, None)),
+                                          order=order)
+                qr = q[rows[0]:rows[-1] + 1]
+                sk, mg = A.skip_set_batched(qr, k, rows, blocks, Bc, 0.1, lam, n_valid, causal)
+                _, sk1, mg1 = A.blasst_tile(qr, k, v, rows, blocks, Bc, 0.1, lam, n_valid, causal)
+                assert np.array_equal(sk, sk1)
+                assert np.allclose(mg, mg1, rtol=0, atol=1e-12) or np.array_equal(mg, mg1)
+                n_skipped += int(sk.sum())
+                if lam > 0.0:
+                    sk2, _ = A.skip_set_vectorized(qr, k, rows, blocks, Bc, 0.1, lam, n_valid, causal)
+                    assert np.array_equal(sk, sk2)
+    assert n_skipped > 0 or order == "descending"    # the sink comes first only in ascending order
