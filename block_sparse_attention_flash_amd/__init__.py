@@ -19,7 +19,8 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``prefill_bwd(q, k, v, out, dout, lse, ...)`` -> (dq, dk, dv) for a static mask;
   ``transpose_block_index(row_ptr, col_idx, Tc)`` -> (col_ptr, row_idx),
   ``prefill_bwd_workspace_size(B, Hq, Nq)``
-* ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor
+* ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor (``noalloc=True``:
+  ``bsattn_decode_fwd_noalloc``, the library's fixed scratch instead of a workspace)
 * ``calibrate_fit(...)``, ``calibrate(target, lengths, lambdas, delta, measure)``,
   ``decode_sparsity(...)``: threshold calibration lambda = a / L
 * ``prefill_plan(...)``, ``decode_plan(...)`` -> Plan: the same calls marshalled
@@ -455,8 +456,11 @@ def decode_split_blocks(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64,
 def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                 Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None,
                 block_state=None, order: str = "ascending", max_scope: str = "sequence",
-                decisions: str = "group") -> Plan:
-    """Marshal a decode (arguments as ``decode_fwd``) into a reusable Plan."""
+                decisions: str = "group", noalloc: bool = False) -> Plan:
+    """Marshal a decode (arguments as ``decode_fwd``) into a reusable Plan.
+    ``noalloc=True`` marshals ``bsattn_decode_fwd_noalloc`` instead: no
+    workspace (the library's fixed per-device scratch holds it; ``out`` must
+    then be given for a call that may allocate nothing at all)."""
     torch = _torch()
     B, Hq, d = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
@@ -467,7 +471,9 @@ def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional
         raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "head dim must be contiguous")
     if out is None:
         out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
-    if workspace is None:
+    if noalloc and workspace is not None:
+        raise BsattnError(_abi.BSATTN_ERR_INVALID_ARG, "the no-allocation decode takes no workspace")
+    if workspace is None and not noalloc:
         workspace = decode_workspace(B, Hq, Hkv, L, d, q.device, Bc, num_splits)
     a = _abi.DecodeArgs()
     a.q, a.k_cache, a.v_cache, a.out = _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out)
@@ -480,28 +486,32 @@ def decode_plan(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional
     a.Bc = int(Bc)
     a.num_splits = int(num_splits)
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    a.workspace_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     a.counters, a.block_state = _ptr(counters), _ptr(block_state)
     a.block_order = _order_code(order)
     a.max_scope = _choice_code("max_scope", max_scope, ("sequence", "split"))
     a.decisions = _choice_code("decisions", decisions, ("group", "head"))
     keep = (q, k_cache, v_cache, workspace, counters, block_state)
-    return Plan(library().bsattn_decode_fwd, a, out, keep)
+    fn = library().bsattn_decode_fwd_noalloc if noalloc else library().bsattn_decode_fwd
+    return Plan(fn, a, out, keep)
 
 
 def decode_fwd(q, k_cache, v_cache, *, L: Optional[int] = None, scale: Optional[float] = None, lam: float = 0.0,
                Bc: int = 64, num_splits: int = 0, workspace=None, out=None, counters=None, block_state=None,
-               order: str = "ascending", max_scope: str = "sequence", decisions: str = "group", stream=None):
+               order: str = "ascending", max_scope: str = "sequence", decisions: str = "group", noalloc: bool = False,
+               stream=None):
     """BLASST decode: q [B, Hq, d] (token at position L-1), caches [B, Lmax, Hkv, d] bf16.
 
     ``workspace`` is a uint8 device tensor of at least
     ``decode_workspace_size`` bytes from ``decode_workspace`` (allocated here if None).
     ``max_scope="split"`` restarts the running max at every split and
     ``decisions="head"`` lets every query head decide for itself (variants;
-    ``block_state`` is then [B, Hq, Tc])."""
+    ``block_state`` is then [B, Hq, Tc]).  ``noalloc=True`` calls
+    ``bsattn_decode_fwd_noalloc`` (no workspace; the library's per-device
+    scratch, up to 32 MiB of workspace)."""
     return decode_plan(q, k_cache, v_cache, L=L, scale=scale, lam=lam, Bc=Bc, num_splits=num_splits,
                        workspace=workspace, out=out, counters=counters, block_state=block_state,
-                       order=order, max_scope=max_scope, decisions=decisions)(stream)
+                       order=order, max_scope=max_scope, decisions=decisions, noalloc=noalloc)(stream)
 
 
 def calibrate_fit(target: float, lengths, lambdas, sparsity, delta: float):
@@ -541,7 +551,9 @@ def decode_sparsity(q, k_cache, v_cache, *, lam: float, L: Optional[int] = None,
 
 
 def decode_check(workspace) -> int:
-    """Health word of the last decode on this workspace (synchronous read): 0 = fine."""
+    """Health word of the last decode on this workspace (synchronous read and
+    clear): 0 = fine.  ``None`` reads the no-allocation decode's scratch on
+    the current device."""
     h = C.c_int32(0)
     _check(library().bsattn_decode_check(C.c_void_p(_ptr(workspace)), C.byref(h)))
     return int(h.value)

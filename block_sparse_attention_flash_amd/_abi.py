@@ -25,7 +25,7 @@ EXPORTED = (
     "bsattn_transpose_block_index", "bsattn_prefill_bwd_workspace_size", "bsattn_prefill_bwd",
     "bsattn_block_index_from_matrix", "bsattn_block_index_from_bitmap", "bsattn_block_index_from_coo",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
-    "bsattn_decode_fwd", "bsattn_decode_check",
+    "bsattn_decode_fwd", "bsattn_decode_check", "bsattn_decode_fwd_noalloc",
     "bsattn_calibrate_threshold",
 )
 
@@ -135,6 +135,8 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_decode_split_blocks.argtypes = [C.c_int32] * 7
     lib.bsattn_decode_fwd.restype = C.c_int
     lib.bsattn_decode_fwd.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
+    lib.bsattn_decode_fwd_noalloc.restype = C.c_int
+    lib.bsattn_decode_fwd_noalloc.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
     lib.bsattn_decode_check.restype = C.c_int
     lib.bsattn_decode_check.argtypes = [C.c_void_p, C.POINTER(C.c_int32)]
     lib.bsattn_calibrate_threshold.restype = C.c_int

@@ -302,15 +302,13 @@ int32_t bsattn_decode_split_blocks(int32_t B, int32_t Hq, int32_t Hkv, int32_t L
   return bps;
 }
 
-bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
-  clear_error();
-  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
-  if (!a->q || !a->k_cache || !a->v_cache || !a->out || !a->workspace)
-    return fail(BSATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, out, workspace must be non-NULL");
+// Validation and parameters shared by the decode entry points (the
+// workspace itself is checked by each caller).
+static bsattn_status decode_prepare(const bsattn_decode_args* a, DecodeParams& p, DecodeWorkspace& w) {
+  if (!a->q || !a->k_cache || !a->v_cache || !a->out)
+    return fail(BSATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, out must be non-NULL");
   if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->out))
     return fail(BSATTN_ERR_UNSUPPORTED, "q, k_cache, v_cache, out must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
-    return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->L < 1 || a->Lmax < a->L)
     return fail(BSATTN_ERR_INVALID_ARG, "need B, Hq, Hkv >= 1 and 1 <= L <= Lmax");
   if (a->Hq % a->Hkv != 0) return fail(BSATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
@@ -325,7 +323,7 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   if ((st = check_strides("q", a->q_stride, 2, 8)) != BSATTN_OK) return st;
   if ((st = check_strides("kv", a->kv_stride, 3, 8)) != BSATTN_OK) return st;
   if ((st = check_strides("out", a->o_stride, 2, 8)) != BSATTN_OK) return st;
-  DecodeParams p{};
+  p = DecodeParams{};
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.out = a->out;
   p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.L = a->L; p.d = a->d; p.G = G;
   p.qs_b = a->q_stride[0]; p.qs_h = a->q_stride[1];
@@ -335,22 +333,60 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
   p.Tc = (a->L + a->Bc - 1) / a->Bc;
   p.num_splits = decode_choose_splits(a->B, a->Hkv, p.Tc, G, a->num_splits, &p.blocks_per_split);
   if (a->block_order != 0 && a->block_order != 1) return fail(BSATTN_ERR_INVALID_ARG, "block_order must be 0 or 1");
-  const DecodeWorkspace w = decode_workspace_layout(a->B, a->Hq, a->Hkv, a->d, p.num_splits);
-  if (a->workspace_bytes < w.total)
-    return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
+  w = decode_workspace_layout(a->B, a->Hq, a->Hkv, a->d, p.num_splits);
   if ((int64_t)a->B * a->Hkv * p.num_splits > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
-  p.workspace = a->workspace; p.counters = a->counters; p.block_state = a->block_state;
+  p.counters = a->counters; p.block_state = a->block_state;
   p.block_order = a->block_order;
   if (a->max_scope != 0 && a->max_scope != 1) return fail(BSATTN_ERR_INVALID_ARG, "max_scope must be 0 or 1");
   if (a->decisions != 0 && a->decisions != 1) return fail(BSATTN_ERR_INVALID_ARG, "decisions must be 0 or 1");
   p.split_reset = a->max_scope;
   p.per_head = a->decisions;
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_decode_fwd(const bsattn_decode_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
+  if (!a->workspace) return fail(BSATTN_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  DecodeParams p;
+  DecodeWorkspace w;
+  bsattn_status st = decode_prepare(a, p, w);
+  if (st != BSATTN_OK) return st;
+  if (a->workspace_bytes < w.total)
+    return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
+  p.workspace = a->workspace;
+  return hip_status(launch_decode(p, stream), "decode launch");
+}
+
+bsattn_status bsattn_decode_fwd_noalloc(const bsattn_decode_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(BSATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->workspace || a->workspace_bytes)
+    return fail(BSATTN_ERR_INVALID_ARG, "the no-allocation decode takes no workspace (workspace must be NULL, "
+                                        "workspace_bytes 0)");
+  DecodeParams p;
+  DecodeWorkspace w;
+  bsattn_status st = decode_prepare(a, p, w);
+  if (st != BSATTN_OK) return st;
+  if (w.total > kNoAllocScratchBytes)
+    return fail(BSATTN_ERR_CAPACITY, "this decode needs %zu bytes of scratch; the no-allocation call has %zu "
+                "(fewer splits, sequences or heads per call fit)", w.total, kNoAllocScratchBytes);
+  void* ptr = nullptr;
+  const int e = noalloc_scratch(&ptr);
+  if (e != 0) return hip_status(e, "no-allocation scratch lookup");
+  p.workspace = ptr;
   return hip_status(launch_decode(p, stream), "decode launch");
 }
 
 bsattn_status bsattn_decode_check(void* workspace, int32_t* health_out) {
   clear_error();
-  if (!workspace || !health_out) return fail(BSATTN_ERR_INVALID_ARG, "workspace and health_out must be non-NULL");
+  if (!health_out) return fail(BSATTN_ERR_INVALID_ARG, "health_out must be non-NULL");
+  if (!workspace) {  // the no-allocation decode's scratch on the current device
+    const int e = noalloc_scratch(&workspace);
+    if (e != 0) return hip_status(e, "no-allocation scratch lookup");
+  }
   int32_t h = 0;
   char* word = static_cast<char*>(workspace) + sizeof(int32_t);
   hipError_t e = hipMemcpy(&h, word, sizeof(int32_t), hipMemcpyDeviceToHost);

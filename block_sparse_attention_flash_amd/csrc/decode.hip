@@ -45,10 +45,50 @@
 // a single address.  Every wait is also bounded; a timed-out wait sets the
 // workspace health word instead of hanging.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace bsattn {
+
+// ---------------------------------------------------------------------------
+// Scratch of bsattn_decode_fwd_noalloc: the decode workspace (health header,
+// tickets, flags, split aggregates, partials) in a fixed device array of the
+// library's code object, for callers that cannot allocate device memory.
+// Each GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+// The array starts zeroed (the health word must), and every call clears the
+// tickets and flags it uses; calls on one GPU share it and must not overlap.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
+
 namespace {
 
 constexpr int NT = 256;

@@ -135,6 +135,11 @@ DecodeWorkspace decode_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int3
 int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int32_t requested,
                              int32_t* blocks_per_split);
 
+// Fixed device scratch of the no-allocation decode (decode.hip): its size,
+// and its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+int noalloc_scratch(void** ptr);
+
 // Kernel launchers (HIP translation units).  Return hipError_t as int.
 int launch_prefill_bf16(const PrefillParams& p, void* stream);
 int launch_prefill_f32(const PrefillParams& p, void* stream);

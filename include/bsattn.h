@@ -396,9 +396,28 @@ bsattn_status bsattn_decode_fwd(const bsattn_decode_args* args, void* stream);
 
 /* Read and clear the decode workspace health word after the stream has
  * finished (host call, synchronous copies): 0 = fine, else a kernel-side wait
- * timed out in a call since the previous check, and that call's output is not
- * valid. */
+ * timed out (bit 0) or a split ticket fell out of range (bit 1) in a call
+ * since the previous check, and that call's output is not valid.
+ * workspace = NULL reads the scratch of bsattn_decode_fwd_noalloc on the
+ * current device. */
 bsattn_status bsattn_decode_check(void* workspace, int32_t* health_out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as bsattn_decode_fwd, but the workspace is a fixed scratch array of
+ * 32 MiB that the library's code object holds on each GPU it runs on, from
+ * the first call on that device (current device; the stream must belong to
+ * it) until the process ends.  args->workspace must be NULL and
+ * args->workspace_bytes 0 (else BSATTN_ERR_INVALID_ARG).  A call whose
+ * workspace (bsattn_decode_workspace_size) exceeds 32 MiB returns
+ * BSATTN_ERR_CAPACITY before enqueueing anything; for scale, 32 sequences x
+ * 8 K/V heads x 131072 keys at d = 128 with automatic splits need about
+ * 20 MiB.  No device memory is allocated or freed by the call.  Every call on
+ * one GPU shares that GPU's scratch, and each call clears the tickets and
+ * flags it uses: calls that overlap on one GPU (different streams without
+ * ordering, several host threads) race and give undefined results.  Its
+ * health word is read with bsattn_decode_check(NULL, ...). */
+bsattn_status bsattn_decode_fwd_noalloc(const bsattn_decode_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* threshold calibration (host only)                                          */

@@ -189,3 +189,19 @@ def test_decode_split_policy():
     assert bsa.decode_split_blocks(1, 4, 3, 64, 128) == 0                        # Hq % Hkv != 0
     assert bsa.decode_workspace_size(32, 32, 8, 131072, 128) > 32 * 8 * 32 * 4 * 128 * 4   # partial O of every split
     assert bsa.decode_workspace_size(0, 1, 1, 1, 64) == 0
+
+
+def test_decode_noalloc_rejects_on_the_host():
+    """bsattn_decode_fwd_noalloc refuses a workspace argument and a call whose
+    workspace would exceed its fixed scratch, before anything is enqueued."""
+    lib = bsa.library()
+    a = _good_decode()
+    assert lib.bsattn_decode_fwd_noalloc(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG   # workspace given
+    a.workspace, a.workspace_bytes = None, 0
+    a.B, a.Hq, a.Hkv, a.L, a.Lmax = 64, 32, 8, 131072, 131072                               # ~40 MiB of workspace
+    assert bsa.decode_workspace_size(64, 32, 8, 131072, 128) > 32 << 20
+    assert lib.bsattn_decode_fwd_noalloc(C.byref(a), None) == _abi.BSATTN_ERR_CAPACITY
+    assert b"scratch" in lib.bsattn_last_error()
+    a.lam = 2.0                                                                             # ordinary validation
+    assert lib.bsattn_decode_fwd_noalloc(C.byref(a), None) == _abi.BSATTN_ERR_INVALID_ARG
+    assert lib.bsattn_decode_fwd_noalloc(None, None) == _abi.BSATTN_ERR_INVALID_ARG
