@@ -17,10 +17,13 @@ its own events (a second pass of K steps), the figure the profiler's kernel
 trace reports.
 
 Prints ONE JSON line.  ``value`` is the dense-equivalent attention TFLOP/s of
-the primary workload (the multimodal DiT image+text configuration by
-default); ``also`` carries the same measurement for the other full-size
-workloads (video DiT static mask, BLASST causal prefill, BLASST decode in
-HBM GB/s), each with its roofline and its share of skipped blocks.
+the primary workload (the BLASST causal GQA 32/8 prefill at 32K tokens by
+default, the largest prefill and the dominant kernel); ``also`` carries the
+same measurement for the other full-size workloads (multimodal DiT
+image+text and video DiT static masks, BLASST decode in HBM GB/s), each with
+its roofline, its share of skipped blocks and its own ``cpu_baseline``: the
+float64 oracle timed on the host cores on a bounded sample of that workload
+and extrapolated to the whole of it.
 
 Definitions:
 * dense-equivalent FLOPs = 4 B Hq d x (allowed query-key pairs of the full
@@ -254,7 +257,7 @@ def run_backward_workload(name: str, steps: int, warmup: int):
 
 # ---------------------------------------------------------------------------- decode
 
-def run_decode_workload(name: str, steps: int, warmup: int):
+def run_decode_workload(name: str, steps: int, warmup: int, keep_inputs: bool = False):
     import torch
     import block_sparse_attention_flash_amd as bsa
     from workloads import get_config, gen_decode_inputs
@@ -280,6 +283,7 @@ def run_decode_workload(name: str, steps: int, warmup: int):
     visited, skipped = int(c[0]), int(c[1])
     log(f"{name}: timing {steps} steps")
     t = time_launches(call, steps, warmup)
+    health_after = bsa.decode_check(ws)          # every timed launch's look-back waits ended in time
     blk_bytes = cfg.Bc * cfg.d * 2
     algo = visited * blk_bytes + (visited - skipped) * blk_bytes + 2 * cfg.B * cfg.Hq * cfg.d * 2
     ms = t["ms_per_step"]
@@ -292,7 +296,7 @@ def run_decode_workload(name: str, steps: int, warmup: int):
         "pct_blocks_skipped": 100.0 * skipped / max(1, visited),
         "blocks": {"visited": visited, "skipped": skipped, "computed": visited - skipped},
         "lambda": cfg.lam, "num_splits": bsa.decode_num_splits(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.Bc),
-        "health": health,
+        "health": health, "health_after_timing": health_after,
         "config": {"workload": f"{name}: {cfg.description}", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "L": cfg.L, "d": cfg.d,
                    "Bc": cfg.Bc, "lambda": cfg.lam, "dtype": "bf16"},
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
@@ -300,6 +304,8 @@ def run_decode_workload(name: str, steps: int, warmup: int):
                      "per_launch_bytes": algo,
                      "traffic": traffic_for("decode_split_kernel", name)},
     }
+    if keep_inputs:
+        res["_inputs"] = (cfg, q, kc, vc)
     del q, kc, vc, out, ws
     torch.cuda.empty_cache()
     return res
@@ -308,6 +314,7 @@ def run_decode_workload(name: str, steps: int, warmup: int):
 # ---------------------------------------------------------------------------- lambda sweep
 
 SWEEP_LAMBDAS = {
+    "cfg4_sink": [0.0, 0.3, 0.35, 0.4, 0.45, 0.5, 0.6, 0.7],
     "cfg4": [0.0, 40.0 / 32768, 1e-2, 3e-2, 0.1, 0.2, 0.3, 0.5],
     "cfg2": [0.0, 1e-2, 0.05, 0.1, 0.3],
     "cfg3": [0.0, 1e-2, 0.1, 0.3],
@@ -557,6 +564,29 @@ def probe_peaks(steps: int = 20, warmup: int = 5):
     return out
 
 
+def host_info():
+    """Host cores available to this process, the BLAS threads the oracle's
+    numpy products use, torch's CPU threads, and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"), default=1)
+    except Exception:
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import torch
+    return {"host_cores_available": cores, "blas_threads": blas, "torch_cpu_threads": torch.get_num_threads(),
+            "cpu_model": model}
+
+
 def cpu_baseline_prefill(res, budget_s: float):
     """Time the float64 oracle (as it stands) on a bounded sample of the same
     workload's (batch, head, tile) items and extrapolate by processed blocks."""
@@ -584,19 +614,45 @@ def cpu_baseline_prefill(res, budget_s: float):
             break
     el = time.perf_counter() - t0
     est = el * res["blocks"]["visited"] / max(1, done_blocks)
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"), default=1)
-    except Exception:
-        blas = None
-    cores = len(os.sched_getaffinity(0))
+    info = host_info()
     dense = res["value"] * res["ms_per_step"] * 1e-3 * 1e12
-    return {"value": dense / est / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": blas or cores,
-            "host_cores_available": cores, "kind": "oracle",
+    return {"value": dense / est / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+            "cores": info["blas_threads"] or info["host_cores_available"], "kind": "oracle",
             "sample": f"{n_items} of {len(items)} (batch, head, tile) items of {res['workload']} in "
                       f"{el:.1f} s, {done_blocks} of {res['blocks']['visited']} visited blocks; full-workload "
                       f"time extrapolated by visited blocks to {est:.1f} s",
-            "method": f"oracle.attention.prefill_tile(method={method!r}), float64 numpy"}
+            "measured_s": el, "extrapolated_s": est,
+            "method": f"oracle.attention.prefill_tile(method={method!r}), float64 numpy", **info}
+
+
+def cpu_baseline_decode(res, budget_s: float):
+    """Time the float64 decode oracle (closed form of Algorithm 1 per sequence
+    and K/V head) on whole sequences until the budget is spent, and
+    extrapolate by sequences to the batch."""
+    from oracle import attention as A
+    cfg, q, kc, vc = res["_inputs"]
+    n_seq = 0
+    t_oracle = 0.0
+    t0 = time.perf_counter()
+    for b in range(cfg.B):
+        qb, kb, vb = q[b].cpu(), kc[b].cpu(), vc[b].cpu()        # one sequence on the host at a time
+        t1 = time.perf_counter()
+        A.decode_sequence(qb, kb, vb, cfg.Bc, cfg.scale, cfg.lam, "closed_form")
+        t_oracle += time.perf_counter() - t1
+        n_seq += 1
+        del qb, kb, vb
+        if time.perf_counter() - t0 > budget_s:
+            break
+    est = t_oracle * cfg.B / n_seq
+    info = host_info()
+    algo = res["roofline"]["per_launch_bytes"]
+    return {"value": algo / est / 1e9, "unit": "GB/s (algorithmic HBM bytes)",
+            "cores": info["blas_threads"] or info["host_cores_available"], "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.B} sequences (all {cfg.Hkv} K/V heads each) of {res['workload']}: "
+                      f"{t_oracle:.1f} s in the oracle (host copies excluded); batch time extrapolated by "
+                      f"sequences to {est:.1f} s",
+            "measured_s": t_oracle, "extrapolated_s": est,
+            "method": "oracle.attention.decode_sequence(method='closed_form'), float64 numpy", **info}
 
 
 def main(argv=None) -> int:
@@ -605,15 +661,17 @@ def main(argv=None) -> int:
     # an 80 us kernel needs a few hundred launches before the clocks settle
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
-    ap.add_argument("--also", default="cfg3,cfg4,cfg5", help="comma list of further workloads ('' for none)")
+    ap.add_argument("--workload", default="cfg4", choices=["cfg2", "cfg3", "cfg4", "cfg5", "cfg4_sink"])
+    ap.add_argument("--also", default="cfg2,cfg3,cfg5", help="comma list of further workloads ('' for none)")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="one work-group per tile (no long-tile cutting)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per workload")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the metric line: a lambda sweep (static + dynamic skipping together) per "
                          "workload, as one JSON line")
+    ap.add_argument("--sweep-only", default="", help="with --sweep: comma list of workloads to sweep (no variants "
+                                                     "or calibration)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the metric line: the static block-sparse backward on the prefill workloads")
     ap.add_argument("--variants", action="store_true",
@@ -637,16 +695,30 @@ def main(argv=None) -> int:
 
     def run(name, keep=False):
         if name == "cfg5":
-            return run_decode_workload(name, a.steps, a.warmup)
+            return run_decode_workload(name, a.steps, a.warmup, keep_inputs=keep)
         return run_prefill_workload(name, a.steps, a.warmup, keep_inputs=keep, use_schedule=not a.no_schedule)
+
+    def with_baseline(name):
+        r = run(name, keep=not a.no_cpu_baseline)
+        if "_inputs" in r:
+            log(f"{name}: oracle baseline on host cores (~{a.cpu_seconds:.0f} s)")
+            r["cpu_baseline"] = (cpu_baseline_decode if name == "cfg5" else cpu_baseline_prefill)(r, a.cpu_seconds)
+            r.pop("_inputs")
+        torch.cuda.empty_cache()
+        return r
 
     torch.cuda.synchronize()
     if a.sweep:
         rep = []
         for name, lams in SWEEP_LAMBDAS.items():
+            if a.sweep_only and name not in a.sweep_only.split(","):
+                continue
             fn = sweep_decode if name == "cfg5" else sweep_prefill
             rep.append(fn(name, lams, min(a.steps, 50) if name != "cfg2" else a.steps, min(a.warmup, 20)
                           if name != "cfg2" else a.warmup))
+        if a.sweep_only:
+            print(json.dumps({"sweep": rep, "steps": a.steps, "device": torch.cuda.get_device_name(0)}))
+            return 0
         var = decode_variants("cfg5", [40.0 / 131072, 1e-2, 0.1], min(a.steps, 50), min(a.warmup, 20))
         cal = calibration_demo()
         print(json.dumps({"sweep": rep, "decode_variants": var, "calibration": cal, "steps": a.steps,
@@ -673,19 +745,12 @@ def main(argv=None) -> int:
         log("copy calibration: 3 copies of 1 GiB (reads 1 GiB, writes 1 GiB each)")
         del src, dst
         torch.cuda.empty_cache()
-    prim = run(a.workload, keep=not a.no_cpu_baseline)
-    cpu = None
-    if not a.no_cpu_baseline and "_inputs" in prim:
-        log(f"oracle baseline on host cores (~{a.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline_prefill(prim, a.cpu_seconds)
-    prim.pop("_inputs", None)
-    torch.cuda.empty_cache()
+    prim = with_baseline(a.workload)
+    cpu = prim.pop("cpu_baseline", None)
     also = []
     if not a.no_also and a.also:
         for name in [x for x in a.also.split(",") if x and x != a.workload]:
-            r = run(name)
-            r.pop("_inputs", None)
-            also.append(r)
+            also.append(with_baseline(name))
     line = {
         "metric": METRIC, "value": prim["value"], "unit": prim["unit"].split(" ")[0],
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": prim["ms_per_step"],

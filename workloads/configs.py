@@ -170,8 +170,19 @@ def _cfg5() -> DecodeWorkload:
         B=32, Hq=32, Hkv=8, L=L, d=128, Bc=64, lam=40.0 / L, seed=5)
 
 
+def _cfg4_sink() -> PrefillWorkload:
+    """The causal GQA 32/8 prefill shape with the "sink" test recipe, whose
+    tiles really skip at moderate lambda (the speed-up against sparsity curve)."""
+    c = _cfg4()
+    return PrefillWorkload(
+        name="cfg4_sink", description="causal GQA 32/8, d128, L32768, sink recipe (skips whole tiles at lambda 0.3-0.7)",
+        dtype="bf16", B=c.B, Hq=c.Hq, Hkv=c.Hkv, N=c.N, d=c.d, Br=128, Bc=64, causal=True, lam=0.5,
+        mask=None, seed=c.seed, generator="sink")
+
+
 CONFIGS = {"cfg1": _cfg1, "cfg2": _cfg2, "cfg3": _cfg3, "cfg4": _cfg4, "cfg5": _cfg5}
+EXTRA = {"cfg4_sink": _cfg4_sink}
 
 
 def get_config(name: str):
-    return CONFIGS[name]()
+    return CONFIGS[name]() if name in CONFIGS else EXTRA[name]()
