@@ -315,8 +315,15 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     mrg = item[4];
   } else {
     t = p.tile_order ? p.tile_order[rank] : (CAUSAL ? p.Tr - 1 - rank : rank);
-    e0 = p.row_ptr ? p.row_ptr[t] : 0;
-    e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
+    // a branch, not two selects: the compiler turns a select between a CSR
+    // entry and p.Tc into one load through a select of the two addresses,
+    // which needs a private copy of p.Tc and a flat load
+    e0 = 0;
+    e1 = p.Tc;
+    if (p.row_ptr) {
+      e0 = p.row_ptr[t];
+      e1 = p.row_ptr[t + 1];
+    }
   }
   // the work item is wave-uniform: keep it (and all block-index arithmetic
   // derived from it) in scalar registers
@@ -548,8 +555,13 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
       if (wave_all) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's word is in LDS
         const uint32_t yes = 2u * it + 1u;
+        const uint32_t vote_addr = lds_addr(sm.vote[0]);
         for (;;) {
-          const u32x4 w = *reinterpret_cast<const volatile u32x4*>(sm.vote[0]);
+          // an LDS read, waited for in place: a volatile read through a
+          // generic pointer becomes a flat load, whose vmcnt wait would also
+          // drain the next block's K/V loads
+          u32x4 w;
+          asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(w) : "v"(vote_addr) : "memory");
           if (w[0] == yes - 1 || w[1] == yes - 1 || w[2] == yes - 1 || w[3] == yes - 1) break;  // kept
           if (w[0] == yes && w[1] == yes && w[2] == yes && w[3] == yes) {
             skip = true;
