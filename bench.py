@@ -133,7 +133,7 @@ def run_prefill_workload(name: str, steps: int, warmup: int, keep_inputs: bool =
         rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
         order_h = bsa.tile_order_lpt(rp_h)
         if use_schedule:
-            sched = bsa.build_schedule(rp_h, bsa.default_max_blocks_per_item(rp_h, cfg.B, cfg.Hq))
+            sched = bsa.default_schedule(rp_h, cfg.B, cfg.Hq, cfg.Hkv, cfg.d)
         build_ms = (time.perf_counter() - t0) * 1e3
         rp, ci, order = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, order_h))
         if sched is not None:
@@ -342,7 +342,7 @@ def sweep_prefill(name: str, lams, steps: int, warmup: int):
     if cfg.mask is not None:
         rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
         order_h = bsa.tile_order_lpt(rp_h)
-        sched = bsa.build_schedule(rp_h, bsa.default_max_blocks_per_item(rp_h, cfg.B, cfg.Hq)).to(dev)
+        sched = bsa.default_schedule(rp_h, cfg.B, cfg.Hq, cfg.Hkv, cfg.d).to(dev)
         rp, ci, order = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, order_h))
         if sched.n_slots:
             ws = bsa.prefill_workspace(cfg.B, cfg.Hq, cfg.d, sched.n_slots, dev)

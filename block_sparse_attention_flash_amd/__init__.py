@@ -13,7 +13,10 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``block_index_from_matrix(m)``, ``block_index_from_bitmap(bits, Tr, Tc)``,
   ``block_index_from_coo(rows, cols, Tr, Tc)`` -> (row_ptr, col_idx)
 * ``tile_order_lpt(row_ptr)`` -> int32 numpy launch order
-* ``build_schedule(row_ptr, max_blocks_per_item)`` -> Schedule (host arrays, counts)
+* ``build_schedule(row_ptr, max_blocks_per_item, order="longest_first")`` -> Schedule
+  (host arrays, counts); ``order="tile"`` applies ``bsattn_schedule_tile_order``;
+  ``prefill_group_major(B, Hq, Hkv, d, n_units)``; ``default_schedule(row_ptr, B, Hq, Hkv, d)``
+  (chunk bound and order chosen for the launch)
 * ``prefill_workspace_size(B, Hq, d, n_slots)``, ``prefill_workspace(...)`` (zero-filled)
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
 * ``prefill_bwd(q, k, v, out, dout, lse, ...)`` -> (dq, dk, dv) for a static mask;
@@ -42,7 +45,7 @@ from . import _abi
 __all__ = [
     "BsattnError", "library", "build_block_index", "validate_block_index", "tile_order_lpt",
     "block_index_from_matrix", "block_index_from_bitmap", "block_index_from_coo",
-    "Schedule", "build_schedule", "default_max_blocks_per_item", "prefill_workspace_size", "prefill_workspace",
+    "Schedule", "build_schedule", "default_max_blocks_per_item", "default_schedule", "prefill_group_major", "prefill_workspace_size", "prefill_workspace",
     "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_plan", "prefill_bwd_workspace_size", "transpose_block_index",
     "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits",
     "decode_split_blocks", "decode_check",
@@ -213,7 +216,11 @@ def default_max_blocks_per_item(row_ptr, B: int, Hq: int, slots: int = 512) -> i
     return max(16, -(-total // (2 * slots)))
 
 
-def build_schedule(row_ptr, max_blocks_per_item: int) -> Schedule:
+def build_schedule(row_ptr, max_blocks_per_item: int, order: str = "longest_first") -> Schedule:
+    """``order``: "longest_first" (the builder's order) or "tile" (cut chunks
+    first, then whole tiles by index: ``bsattn_schedule_tile_order``)."""
+    if order not in ("longest_first", "tile"):
+        raise ValueError(f"order must be 'longest_first' or 'tile', not {order!r}")
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
     Tr = row_ptr.size - 1
     ni, nm, ns = C.c_int32(0), C.c_int32(0), C.c_int32(0)
@@ -225,7 +232,28 @@ def build_schedule(row_ptr, max_blocks_per_item: int) -> Schedule:
     _check(lib.bsattn_build_schedule(row_ptr.ctypes.data, Tr, int(max_blocks_per_item), items.ctypes.data,
                                      ni.value, merges.ctypes.data, merges.shape[0], C.byref(ni), C.byref(nm),
                                      C.byref(ns)))
+    if order == "tile":
+        _check(lib.bsattn_schedule_tile_order(items.ctypes.data, ni.value))
     return Schedule(items, merges[:nm.value].copy(), ns.value)
+
+
+def prefill_group_major(B: int, Hq: int, Hkv: int, d: int, n_units: int) -> bool:
+    """True when a bf16 prefill launch walks each (batch, K/V head) group's
+    work items consecutively (``bsattn_prefill_group_major``)."""
+    r = int(library().bsattn_prefill_group_major(B, Hq, Hkv, d, n_units))
+    if r < 0:
+        raise ValueError(f"invalid prefill shape B={B} Hq={Hq} Hkv={Hkv} d={d} n_units={n_units}")
+    return r == 1
+
+
+def default_schedule(row_ptr, B: int, Hq: int, Hkv: int, d: int) -> Schedule:
+    """Schedule with ``default_max_blocks_per_item``, in tile order when the
+    launch walks groups one at a time (neighbouring tiles then share K/V
+    blocks in L2), longest first otherwise (the shorter tail)."""
+    s = build_schedule(row_ptr, default_max_blocks_per_item(row_ptr, B, Hq))
+    if prefill_group_major(B, Hq, Hkv, d, s.n_items):
+        _check(library().bsattn_schedule_tile_order(s.items.ctypes.data, s.n_items))
+    return s
 
 
 def prefill_workspace_size(B: int, Hq: int, d: int, n_slots: int) -> int:

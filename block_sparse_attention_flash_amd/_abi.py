@@ -21,7 +21,8 @@ BSATTN_FP32 = 1
 EXPORTED = (
     "bsattn_status_string", "bsattn_last_error", "bsattn_version",
     "bsattn_build_block_index", "bsattn_validate_block_index", "bsattn_tile_order_lpt",
-    "bsattn_build_schedule", "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
+    "bsattn_build_schedule", "bsattn_schedule_tile_order", "bsattn_prefill_group_major",
+    "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
     "bsattn_transpose_block_index", "bsattn_prefill_bwd_workspace_size", "bsattn_prefill_bwd",
     "bsattn_block_index_from_matrix", "bsattn_block_index_from_bitmap", "bsattn_block_index_from_coo",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
@@ -109,6 +110,10 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_build_schedule.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
                                           C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32)]
+    lib.bsattn_schedule_tile_order.restype = C.c_int
+    lib.bsattn_schedule_tile_order.argtypes = [C.c_void_p, C.c_int32]
+    lib.bsattn_prefill_group_major.restype = C.c_int32
+    lib.bsattn_prefill_group_major.argtypes = [C.c_int32] * 5
     lib.bsattn_prefill_workspace_size.restype = C.c_size_t
     lib.bsattn_prefill_workspace_size.argtypes = [C.c_int32] * 4
     lib.bsattn_prefill_fwd.restype = C.c_int

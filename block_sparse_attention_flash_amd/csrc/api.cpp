@@ -107,6 +107,14 @@ int32_t decode_choose_splits(int32_t B, int32_t Hkv, int32_t Tc, int32_t G, int3
   return (Tc + bps - 1) / bps;
 }
 
+bool prefill_group_major(int B, int Hq, int Hkv, int d, int64_t units) {
+  // groups divide into the 8 XCDs, and one XCD (32 CUs) has at least four
+  // waves of resident work-groups
+  if (((int64_t)B * Hkv) % 8 != 0) return false;
+  const int64_t grid = (int64_t)B * Hq * units;
+  return grid / 8 >= 4 * 32 * (d == 64 ? kPrefillWgPerCu64 : kPrefillWgPerCu128);
+}
+
 }  // namespace bsattn
 
 using namespace bsattn;
@@ -269,6 +277,11 @@ bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream)
       (int64_t)p.B * p.Hq * p.Nq > 0x7fffffffLL)
     return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   return hip_status(launch_prefill_bwd(p, stream), "prefill backward launch");
+}
+
+int32_t bsattn_prefill_group_major(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t n_units) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || n_units < 1 || Hq % Hkv || (d != 64 && d != 128)) return -1;
+  return prefill_group_major(B, Hq, Hkv, d, n_units) ? 1 : 0;
 }
 
 size_t bsattn_prefill_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t n_slots) {

@@ -381,6 +381,25 @@ bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t 
   return BSATTN_OK;
 }
 
+bsattn_status bsattn_schedule_tile_order(int32_t* items, int32_t n_items) {
+  using namespace bsattn;
+  clear_error();
+  if (n_items < 0 || (n_items > 0 && !items)) return fail(BSATTN_ERR_INVALID_ARG, "items NULL or n_items < 0");
+  struct Item { int32_t f[5]; };
+  std::vector<Item> it(n_items);
+  std::memcpy(it.data(), items, (size_t)n_items * sizeof(Item));
+  for (const Item& x : it)
+    if ((x.f[3] < 0) != (x.f[4] < 0)) return fail(BSATTN_ERR_INVALID_ARG, "item with slot %d but merge %d", x.f[3], x.f[4]);
+  // chunks of cut tiles first, in their present order; then whole tiles by index
+  std::stable_sort(it.begin(), it.end(), [](const Item& x, const Item& y) {
+    const bool cx = x.f[3] >= 0, cy = y.f[3] >= 0;
+    if (cx != cy) return cx;
+    return !cx && x.f[0] < y.f[0];
+  });
+  std::memcpy(items, it.data(), (size_t)n_items * sizeof(Item));
+  return BSATTN_OK;
+}
+
 bsattn_status bsattn_tile_order_lpt(const int32_t* row_ptr, int32_t Tr, int32_t* order) {
   using namespace bsattn;
   clear_error();

@@ -142,6 +142,13 @@ int noalloc_scratch(void** ptr);
 
 // Kernel launchers (HIP translation units).  Return hipError_t as int.
 int launch_prefill_bf16(const PrefillParams& p, void* stream);
+// Resident work-groups per CU of the bf16 prefill kernel (its launch bounds).
+constexpr int kPrefillWgPerCu64 = 3;
+constexpr int kPrefillWgPerCu128 = 2;
+// Work order of a bf16 prefill launch over `units` work items per head (tiles,
+// or schedule items): true = group-major (each XCD walks one (batch, K/V
+// head) group's items consecutively), false = rank-major.
+bool prefill_group_major(int B, int Hq, int Hkv, int d, int64_t units);
 int launch_prefill_f32(const PrefillParams& p, void* stream);
 int launch_decode(const DecodeParams& p, void* stream);
 

@@ -224,7 +224,7 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // Work-groups per CU the register budget is cut for: three at d = 64 (at most
 // 168 VGPRs), two at d = 128 (at most 256).
 template <int D>
-constexpr int kMinBlocksPerCu = D == 64 ? 3 : 2;
+constexpr int kMinBlocksPerCu = D == 64 ? kPrefillWgPerCu64 : kPrefillWgPerCu128;
 
 // MAXONLY (with DYN): the pass that runs before a skipping launch whose
 // schedule cuts tiles.  Each chunk of a cut tile writes, per query row, the
@@ -794,8 +794,7 @@ hipError_t launch(const PrefillParams& p0, hipStream_t s) {
   PrefillParams p = p0;
   const int64_t units = p.sched_items ? p.n_items : p.Tr;
   const int64_t grid = (int64_t)p.B * p.Hq * units;
-  // rank-major when one XCD (32 CUs) has under four waves of work-groups
-  p.rank_major = grid / 8 < 4 * 32 * kMinBlocksPerCu<D> ? 1 : 0;
+  p.rank_major = prefill_group_major(p.B, p.Hq, p.Hkv, D, units) ? 0 : 1;
   // Cut tiles: the arrival counters sit at offsets that depend on the call's
   // shape (n_slots), so a workspace reused with another shape may hold any
   // bytes there.  A launch before the main one zeroes them: the chunk-maximum

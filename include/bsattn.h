@@ -185,6 +185,31 @@ bsattn_status bsattn_build_schedule(const int32_t* row_ptr, int32_t Tr, int32_t 
                                     int32_t merges_capacity, int32_t* n_items, int32_t* n_merges,
                                     int32_t* n_slots);
 
+/*
+ * Locality order for a schedule (DiT article section 5.3: memory throughput).
+ * Reorders the items of bsattn_build_schedule in place: the chunks of cut
+ * tiles first, in their present order (longest first), then the whole tiles
+ * by ascending tile index, so that work-groups started together hold
+ * neighbouring tiles, whose key blocks overlap, in one L2.  Merges and slots
+ * are unchanged (items keep their fields).  Pays off when a launch walks each
+ * (batch, K/V head) group's items consecutively, see
+ * bsattn_prefill_group_major; otherwise longest first gives the shorter tail.
+ * Host buffer [n_items][5].  INVALID_ARG if an item has a slot but no merge
+ * or the reverse.
+ */
+bsattn_status bsattn_schedule_tile_order(int32_t* items, int32_t n_items);
+
+/*
+ * Work order of a bf16 prefill launch with n_units work items per (batch,
+ * query head): tiles (Tr), or the n_items of a schedule.  Returns 1 when each
+ * XCD walks one (batch, K/V head) group's items consecutively (group-major:
+ * B * Hkv divisible by 8 and enough work-groups for four waves per XCD), 0
+ * when the launch takes items rank by rank across groups, -1 for an invalid
+ * shape (any size < 1, Hq % Hkv != 0, d not 64 or 128).  The launch itself
+ * uses this rule.
+ */
+int32_t bsattn_prefill_group_major(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t n_units);
+
 /* ------------------------------------------------------------------------ */
 /* prefill                                                                    */
 /* ------------------------------------------------------------------------ */

@@ -150,6 +150,48 @@ def test_schedule_covers_every_entry_once():
     assert bsa.build_schedule(rp, 5000).n_slots == 0
 
 
+def test_schedule_tile_order():
+    c3 = get_config("cfg3")
+    rp, _ = bsa.build_block_index(c3.mask, c3.N, c3.N, 128, 64)
+    lpt = bsa.build_schedule(rp, 64)
+    tile = bsa.build_schedule(rp, 64, order="tile")
+    assert tile.n_slots == lpt.n_slots and np.array_equal(tile.merges, lpt.merges)
+    # the same items, each with its fields
+    key = lambda a: sorted(map(tuple, a.tolist()))
+    assert key(tile.items) == key(lpt.items)
+    chunk = tile.items[:, 3] >= 0
+    k = int(chunk.sum())
+    assert k > 0 and chunk[:k].all() and not chunk[k:].any()            # chunks first
+    assert np.array_equal(tile.items[:k], lpt.items[lpt.items[:, 3] >= 0])  # in their longest-first order
+    assert (np.diff(tile.items[k:, 0]) > 0).all()                        # whole tiles ascending
+    with pytest.raises(ValueError):
+        bsa.build_schedule(rp, 64, order="random")
+    bad = np.array([[0, 0, 1, 0, -1]], np.int32)                         # a slot without a merge
+    assert bsa.library().bsattn_schedule_tile_order(bad.ctypes.data, 1) != 0
+
+
+def test_prefill_group_major():
+    c2, c3 = get_config("cfg2"), get_config("cfg3")
+    rp2, _ = bsa.build_block_index(c2.mask, c2.N, c2.N, 128, 64)
+    rp3, _ = bsa.build_block_index(c3.mask, c3.N, c3.N, 128, 64)
+    s2 = bsa.default_schedule(rp2, c2.B, c2.Hq, c2.Hkv, c2.d)
+    s3 = bsa.default_schedule(rp3, c3.B, c3.Hq, c3.Hkv, c3.d)
+    # multimodal DiT image+text: too few work-groups per XCD, rank by rank, longest first
+    assert not bsa.prefill_group_major(c2.B, c2.Hq, c2.Hkv, c2.d, s2.n_items)
+    lens = (s2.items[:, 2] - s2.items[:, 1]).tolist()
+    assert lens == sorted(lens, reverse=True)
+    # video DiT: many waves of work-groups per XCD, group by group, tile order
+    assert bsa.prefill_group_major(c3.B, c3.Hq, c3.Hkv, c3.d, s3.n_items)
+    k = int((s3.items[:, 3] >= 0).sum())
+    assert (np.diff(s3.items[k:, 0]) > 0).all()
+    # groups that do not divide into the 8 XCDs, and the threshold: 4 waves of 2 or 3 resident work-groups
+    assert not bsa.prefill_group_major(1, 12, 12, 128, 10000)
+    assert bsa.prefill_group_major(1, 8, 8, 128, 256) and not bsa.prefill_group_major(1, 8, 8, 128, 255)
+    assert bsa.prefill_group_major(1, 8, 8, 64, 384) and not bsa.prefill_group_major(1, 8, 8, 64, 383)
+    with pytest.raises(ValueError):
+        bsa.prefill_group_major(1, 8, 3, 128, 10)
+
+
 def test_schedule_validation():
     import ctypes as C
     from block_sparse_attention_flash_amd import _abi

@@ -115,10 +115,10 @@ def test_cfg4_shape_sink_outputs_sampled(cfg4_sink_run):
 def test_cfg3_schedule_dynamic_full_launch():
     cfg = get_config("cfg3")
     lam = 0.8
-    _say(f"video DiT N65920 d128, static mask + default schedule, lambda {lam}")
+    _say(f"video DiT N65920 d128, static mask + default schedule (tile order), lambda {lam}")
     q, k, v = gen_prefill_inputs(cfg, device=DEV)
     rp, ci = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
-    sched = bsa.build_schedule(rp, bsa.default_max_blocks_per_item(rp, cfg.B, cfg.Hq))
+    sched = bsa.default_schedule(rp, cfg.B, cfg.Hq, cfg.Hkv, cfg.d)
     assert sched.n_merges >= 1
     Tr, Tc = cfg.N // 128, cfg.N // 64
     st = torch.zeros((1, cfg.Hq, Tr, Tc), dtype=torch.uint8, device=DEV)
@@ -152,3 +152,21 @@ def test_cfg3_schedule_dynamic_full_launch():
             check_prefill_tile(qh, kh, vh, oh, st, cnt, 0, h, t, Br=128, Bc=64, scale=cfg.scale, causal=False,
                                lam=lam, n_valid=cfg.mask.n_valid, row_ptr=rp, col_idx=ci,
                                rows_limit=cfg.mask.n_valid)
+
+
+def test_cfg3_schedule_orders_bit_identical():
+    """The launch order of work items changes nothing in the results: the
+    video DiT prefill with its schedule longest first and in tile order."""
+    cfg = get_config("cfg3")
+    _say("video DiT N65920 d128, schedule longest first against tile order, lambda 0")
+    q, k, v = gen_prefill_inputs(cfg, device=DEV)
+    rp, ci = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    mb = bsa.default_max_blocks_per_item(rp, cfg.B, cfg.Hq)
+    rp_d, ci_d = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    outs = []
+    for order in ("longest_first", "tile"):
+        sched = bsa.build_schedule(rp, mb, order=order)
+        outs.append(bsa.prefill_fwd(q, k, v, scale=cfg.scale, row_ptr=rp_d, col_idx=ci_d, n_valid=cfg.mask.n_valid,
+                                    schedule=sched))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
