@@ -207,7 +207,7 @@ def visited_pairs(cfg, rp_h, ci_h):
     return n
 
 
-def run_backward_workload(name: str, steps: int, warmup: int):
+def run_backward_workload(name: str, steps: int, warmup: int, use_schedule: bool = True):
     """The static block-sparse backward (dot, dK/dV, dQ kernels) on a prefill
     workload at lambda = 0, with the forward timed alongside.  Processed
     FLOPs: the dK/dV kernel computes S, dP, dV, dK (4 products) and the dQ
@@ -223,18 +223,23 @@ def run_backward_workload(name: str, steps: int, warmup: int):
     q, k, v = gen_prefill_inputs(cfg, device=dev)
     dout = gen_prefill_grad_output(cfg, device=dev)
     Tc = -(-cfg.N // cfg.Bc)
-    rp = ci = cp = ri = rp_h = ci_h = None
+    rp = ci = cp = ri = rp_h = ci_h = sched = fsched = fws = None
     if cfg.mask is not None:
         rp_h, ci_h = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, cfg.Br, cfg.Bc)
         cp_h, ri_h = bsa.transpose_block_index(rp_h, ci_h, Tc)
         rp, ci, cp, ri = (torch.from_numpy(x).to(dev) for x in (rp_h, ci_h, cp_h, ri_h))
+        if use_schedule:
+            sched = bsa.default_bwd_schedule(rp_h, cp_h, ri_h, cfg.B, cfg.Hq, cfg.Hkv, cfg.d).to(dev)
+            fsched = bsa.default_schedule(rp_h, cfg.B, cfg.Hq, cfg.Hkv, cfg.d).to(dev)
     lse = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
+    if fsched is not None and fsched.n_slots:
+        fws = bsa.prefill_workspace(cfg.B, cfg.Hq, cfg.d, fsched.n_slots, dev)
     fwd = bsa.prefill_plan(q, k, v, scale=cfg.scale, causal=cfg.causal, row_ptr=rp, col_idx=ci,
-                           n_valid=cfg.n_valid, out=out, lse=lse)
+                           n_valid=cfg.n_valid, out=out, lse=lse, schedule=fsched, workspace=fws)
     fwd()
     bwd = bsa.prefill_bwd_plan(q, k, v, out, dout, lse, scale=cfg.scale, causal=cfg.causal, row_ptr=rp,
-                               col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=cfg.n_valid)
+                               col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=cfg.n_valid, schedule=sched)
     torch.cuda.synchronize()
     pairs = visited_pairs(cfg, rp_h, ci_h) * cfg.B * cfg.Hq
     per_gemm = 2 * cfg.Br * cfg.Bc * cfg.d
@@ -243,6 +248,8 @@ def run_backward_workload(name: str, steps: int, warmup: int):
     tf = time_launches(fwd, steps, warmup)
     ms = tb["ms_per_step"]
     res = {"workload": name, "description": cfg.description, "ms_per_step": ms, "timing": tb,
+           "schedule": None if sched is None else {"dq_items": sched.dq.n_items, "dq_slots": sched.dq.n_slots,
+                                                   "kv_items": sched.kv.n_items, "kv_slots": sched.kv.n_slots},
            "forward_ms_per_step": tf["ms_per_step"], "backward_over_forward": ms / tf["ms_per_step"],
            "visited_pairs": pairs,
            "processed_tflops": 7 * per_gemm * pairs / (ms * 1e-3) / 1e12,
@@ -665,7 +672,7 @@ def main(argv=None) -> int:
     ap.add_argument("--also", default="cfg2,cfg3,cfg5", help="comma list of further workloads ('' for none)")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-schedule", action="store_true", help="one work-group per tile (no long-tile cutting)")
+    ap.add_argument("--no-schedule", action="store_true", help="one work-group per tile or key block (no cutting of long ones)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per workload")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the metric line: a lambda sweep (static + dynamic skipping together) per "
@@ -726,7 +733,7 @@ def main(argv=None) -> int:
         return 0
     if a.backward:
         names = [a.workload] + [n for n in (a.also.split(",") if a.also and not a.no_also else []) if n != "cfg5"]
-        rep = [run_backward_workload(n, a.steps, a.warmup) for n in names]
+        rep = [run_backward_workload(n, a.steps, a.warmup, use_schedule=not a.no_schedule) for n in names]
         print(json.dumps({"backward": rep, "device": torch.cuda.get_device_name(0)}))
         return 0
     if a.probe_peaks:

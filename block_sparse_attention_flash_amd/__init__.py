@@ -21,7 +21,9 @@ Entry points (same names as the C ABI, minus the ``bsattn_`` prefix):
 * ``prefill_fwd(q, k, v, ...)`` -> out tensor (async on the current stream)
 * ``prefill_bwd(q, k, v, out, dout, lse, ...)`` -> (dq, dk, dv) for a static mask;
   ``transpose_block_index(row_ptr, col_idx, Tc)`` -> (col_ptr, row_idx),
-  ``prefill_bwd_workspace_size(B, Hq, Nq)``
+  ``prefill_bwd_workspace_size(B, Hq, Hkv, Nq, d, dq_n_slots=0, kv_n_slots=0)``,
+  ``build_dkdv_schedule(col_ptr, row_idx, G, d, max_positions_per_item)``, ``BwdSchedule``,
+  ``default_bwd_schedule(row_ptr, col_ptr, row_idx, B, Hq, Hkv, d)``
 * ``decode_fwd(q, k_cache, v_cache, ...)`` -> out tensor (``noalloc=True``:
   ``bsattn_decode_fwd_noalloc``, the library's fixed scratch instead of a workspace)
 * ``calibrate_fit(...)``, ``calibrate(target, lengths, lambdas, delta, measure)``,
@@ -47,6 +49,7 @@ __all__ = [
     "block_index_from_matrix", "block_index_from_bitmap", "block_index_from_coo",
     "Schedule", "build_schedule", "default_max_blocks_per_item", "default_schedule", "prefill_group_major", "prefill_workspace_size", "prefill_workspace",
     "prefill_fwd", "prefill_plan", "prefill_bwd", "prefill_bwd_plan", "prefill_bwd_workspace_size", "transpose_block_index",
+    "build_dkdv_schedule", "BwdSchedule", "default_bwd_schedule",
     "decode_fwd", "decode_plan", "Plan", "decode_workspace_size", "decode_workspace", "decode_num_splits",
     "decode_split_blocks", "decode_check",
     "calibrate_fit", "calibrate", "decode_sparsity",
@@ -401,13 +404,82 @@ def prefill_fwd(q, k, v, *, scale: Optional[float] = None, lam: float = 0.0, cau
                         workspace=workspace, lse=lse)(stream)
 
 
-def prefill_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
-    return int(library().bsattn_prefill_bwd_workspace_size(B, Hq, Nq))
+def prefill_bwd_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, d: int, dq_n_slots: int = 0,
+                               kv_n_slots: int = 0) -> int:
+    return int(library().bsattn_prefill_bwd_workspace_size(B, Hq, Hkv, Nq, d, dq_n_slots, kv_n_slots))
+
+
+class KvSchedule:
+    """Host arrays of bsattn_build_dkdv_schedule plus their device copies (``to``)."""
+
+    def __init__(self, items, merges, n_slots):
+        self.items, self.merges, self.n_slots = items, merges, int(n_slots)
+        self.d_items = self.d_merges = None
+
+    @property
+    def n_items(self) -> int:
+        return self.items.shape[0]
+
+    @property
+    def n_merges(self) -> int:
+        return self.merges.shape[0]
+
+    def to(self, device):
+        torch = _torch()
+        self.d_items = torch.from_numpy(self.items.reshape(-1)).to(device)
+        self.d_merges = torch.from_numpy(self.merges.reshape(-1)).to(device) if self.n_merges else None
+        return self
+
+
+def build_dkdv_schedule(col_ptr, row_idx, G: int, d: int, max_positions_per_item: int) -> KvSchedule:
+    col_ptr = np.ascontiguousarray(col_ptr, dtype=np.int32)
+    row_idx = np.ascontiguousarray(row_idx, dtype=np.int32)
+    if row_idx.size == 0:
+        row_idx = np.zeros(1, np.int32)
+    Tc = col_ptr.size - 1
+    ni, nm, ns = C.c_int32(0), C.c_int32(0), C.c_int32(0)
+    lib = library()
+    args = (col_ptr.ctypes.data, row_idx.ctypes.data, Tc, int(G), int(d), int(max_positions_per_item))
+    _check(lib.bsattn_build_dkdv_schedule(*args, None, 0, None, 0, C.byref(ni), C.byref(nm), C.byref(ns)))
+    items = np.zeros((ni.value, 8), np.int32)
+    merges = np.zeros((max(1, nm.value), 3), np.int32)
+    _check(lib.bsattn_build_dkdv_schedule(*args, items.ctypes.data, ni.value, merges.ctypes.data, merges.shape[0],
+                                          C.byref(ni), C.byref(nm), C.byref(ns)))
+    return KvSchedule(items, merges[:nm.value].copy(), ns.value)
+
+
+class BwdSchedule:
+    """The backward's two schedules: ``dq`` (a Schedule over the CSR) and
+    ``kv`` (a KvSchedule over the CSC); either may be None."""
+
+    def __init__(self, dq=None, kv=None):
+        self.dq, self.kv = dq, kv
+
+    def to(self, device):
+        for s in (self.dq, self.kv):
+            if s is not None and s.d_items is None:
+                s.to(device)
+        return self
+
+
+def default_bwd_schedule(row_ptr, col_ptr, row_idx, B: int, Hq: int, Hkv: int, d: int,
+                         slots: int = 512) -> BwdSchedule:
+    """Chunk bounds of half the mean work per concurrent work-group slot: dQ
+    as the forward's ``default_max_blocks_per_item``; dK/dV over the (head,
+    tile) positions of every group of key blocks."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int32)
+    dq = build_schedule(row_ptr, default_max_blocks_per_item(row_ptr, B, Hq, slots))
+    G = Hq // Hkv
+    probe = build_dkdv_schedule(col_ptr, row_idx, G, d, 1 << 30)   # one item per group: their sizes
+    total = int((probe.items[:, 2] - probe.items[:, 1]).sum()) * B * Hkv
+    kv = build_dkdv_schedule(col_ptr, row_idx, G, d, max(8, -(-total // (2 * slots))))
+    return BwdSchedule(dq, kv)
 
 
 def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
                      row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
-                     dq=None, dk=None, dv=None, workspace=None, block_state=None) -> Plan:
+                     dq=None, dk=None, dv=None, workspace=None, block_state=None,
+                     schedule: Optional[BwdSchedule] = None) -> Plan:
     """Marshal a backward (arguments as ``prefill_bwd``) into a reusable Plan
     whose call returns (dq, dk, dv)."""
     torch = _torch()
@@ -418,8 +490,14 @@ def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, 
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    sq = schedule.dq if schedule is not None else None
+    sk = schedule.kv if schedule is not None else None
+    if schedule is not None:
+        schedule.to(q.device)
     if workspace is None:
-        workspace = torch.empty(prefill_bwd_workspace_size(B, Hq, Nq), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(prefill_bwd_workspace_size(B, Hq, Hkv, Nq, d, sq.n_slots if sq else 0,
+                                                           sk.n_slots if sk else 0),
+                                dtype=torch.uint8, device=q.device)
     a = _abi.BwdArgs()
     a.dtype = _abi.BSATTN_BF16
     a.q, a.k, a.v, a.out, a.dout = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout)
@@ -439,13 +517,19 @@ def prefill_bwd_plan(q, k, v, out, dout, lse, *, scale: Optional[float] = None, 
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     a.block_state = _ptr(block_state)
-    keep = (q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx, workspace, block_state)
+    if sq is not None:
+        a.dq_items, a.dq_n_items = _ptr(sq.d_items), sq.n_items
+        a.dq_merges, a.dq_n_merges, a.dq_n_slots = _ptr(sq.d_merges), sq.n_merges, sq.n_slots
+    if sk is not None:
+        a.kv_items, a.kv_n_items = _ptr(sk.d_items), sk.n_items
+        a.kv_merges, a.kv_n_merges, a.kv_n_slots = _ptr(sk.d_merges), sk.n_merges, sk.n_slots
+    keep = (q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx, workspace, block_state, schedule)
     return Plan(library().bsattn_prefill_bwd, a, (dq, dk, dv), keep)
 
 
 def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causal: bool = False,
                 row_ptr=None, col_idx=None, col_ptr=None, row_idx=None, n_valid: int = 0,
-                dq=None, dk=None, dv=None, workspace=None, block_state=None, stream=None):
+                dq=None, dk=None, dv=None, workspace=None, block_state=None, schedule=None, stream=None):
     """Gradients of the block-sparse forward for the loss
     sum(out * dout): q, out, dout [B, Nq, Hq, d], k, v [B, Nk, Hkv, d] bf16,
     ``lse`` float32 [B, Hq, Nq] from ``prefill_fwd(..., lse=)``.  The mask
@@ -453,11 +537,12 @@ def prefill_bwd(q, k, v, out, dout, lse, *, scale: Optional[float] = None, causa
     device copies of ``transpose_block_index``.  ``workspace`` (uint8, at
     least ``prefill_bwd_workspace_size`` bytes) is allocated here if None.
     After a forward with lambda > 0, pass its ``block_state`` (uint8
-    [B, Hq, Tr, Tc]): the blocks it skipped get no gradient.  Returns
-    (dq, dk, dv)."""
+    [B, Hq, Tr, Tc]): the blocks it skipped get no gradient.  ``schedule``
+    (a BwdSchedule, e.g. ``default_bwd_schedule``) cuts long tiles and key
+    blocks into chunks.  Returns (dq, dk, dv)."""
     return prefill_bwd_plan(q, k, v, out, dout, lse, scale=scale, causal=causal, row_ptr=row_ptr,
                             col_idx=col_idx, col_ptr=col_ptr, row_idx=row_idx, n_valid=n_valid, dq=dq, dk=dk,
-                            dv=dv, workspace=workspace, block_state=block_state)(stream)
+                            dv=dv, workspace=workspace, block_state=block_state, schedule=schedule)(stream)
 
 
 def decode_workspace_size(B: int, Hq: int, Hkv: int, L: int, d: int, Bc: int = 64, num_splits: int = 0) -> int:

@@ -24,6 +24,7 @@ EXPORTED = (
     "bsattn_build_schedule", "bsattn_schedule_tile_order", "bsattn_prefill_group_major",
     "bsattn_prefill_workspace_size", "bsattn_prefill_fwd",
     "bsattn_transpose_block_index", "bsattn_prefill_bwd_workspace_size", "bsattn_prefill_bwd",
+    "bsattn_build_dkdv_schedule",
     "bsattn_block_index_from_matrix", "bsattn_block_index_from_bitmap", "bsattn_block_index_from_coo",
     "bsattn_decode_workspace_size", "bsattn_decode_num_splits", "bsattn_decode_split_blocks",
     "bsattn_decode_fwd", "bsattn_decode_check", "bsattn_decode_fwd_noalloc",
@@ -72,7 +73,11 @@ class BwdArgs(C.Structure):
                 ("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("col_ptr", C.c_void_p), ("row_idx", C.c_void_p),
                 ("n_valid", C.c_int32), ("scale", C.c_float), ("causal", C.c_int32), ("Br", C.c_int32),
                 ("Bc", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("block_state", C.c_void_p)]
+                ("block_state", C.c_void_p),
+                ("dq_items", C.c_void_p), ("dq_n_items", C.c_int32), ("dq_merges", C.c_void_p),
+                ("dq_n_merges", C.c_int32), ("dq_n_slots", C.c_int32),
+                ("kv_items", C.c_void_p), ("kv_n_items", C.c_int32), ("kv_merges", C.c_void_p),
+                ("kv_n_merges", C.c_int32), ("kv_n_slots", C.c_int32)]
 
 
 class DecodeArgs(C.Structure):
@@ -129,7 +134,11 @@ def load(path: str = None) -> C.CDLL:
     lib.bsattn_transpose_block_index.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
                                                  C.c_void_p]
     lib.bsattn_prefill_bwd_workspace_size.restype = C.c_size_t
-    lib.bsattn_prefill_bwd_workspace_size.argtypes = [C.c_int32] * 3
+    lib.bsattn_prefill_bwd_workspace_size.argtypes = [C.c_int32] * 7
+    lib.bsattn_build_dkdv_schedule.restype = C.c_int
+    lib.bsattn_build_dkdv_schedule.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                               C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+                                               C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
     lib.bsattn_prefill_bwd.restype = C.c_int
     lib.bsattn_prefill_bwd.argtypes = [C.POINTER(BwdArgs), C.c_void_p]
     lib.bsattn_decode_workspace_size.restype = C.c_size_t

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -75,6 +76,20 @@ PrefillWorkspace prefill_workspace_layout(int32_t B, int32_t Hq, int32_t d, int3
   w.cnt = off; off = align256(off + units * 4 * sizeof(int32_t));  // {visited, skipped, rows agreeing, -}
   w.arrive = off; off = align256(off + units * sizeof(int32_t));  // n_merges <= n_slots
   w.pre = off; off = align256(off + units * 128 * kPreSplit * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+BwdWorkspace bwd_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t d, int32_t dq_n_slots,
+                                  int32_t kv_n_slots) {
+  BwdWorkspace w{};
+  const int32_t NB = d == 64 ? kDkdvBlocks64 : kDkdvBlocks128;
+  size_t off = 0;
+  w.dvec = off;      off = align256(off + (size_t)B * Hq * Nq * sizeof(float));
+  w.dq_part = off;   off = align256(off + (size_t)dq_n_slots * B * Hq * 128 * d * sizeof(float));
+  w.dq_arrive = off; off = align256(off + (size_t)dq_n_slots * B * Hq * sizeof(int32_t));  // n_merges <= n_slots
+  w.kv_part = off;   off = align256(off + (size_t)kv_n_slots * B * Hkv * NB * 64 * 2 * d * sizeof(float));
+  w.kv_arrive = off; off = align256(off + (size_t)kv_n_slots * B * Hkv * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -217,9 +232,10 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* a, void* stream) {
   return hip_status(e, "prefill launch");
 }
 
-size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Nq) {
-  if (B < 1 || Hq < 1 || Nq < 1) return 0;
-  return align256((size_t)B * Hq * Nq * sizeof(float));
+size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t d,
+                                         int32_t dq_n_slots, int32_t kv_n_slots) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || (d != 64 && d != 128) || dq_n_slots < 0 || kv_n_slots < 0) return 0;
+  return bwd_workspace_layout(B, Hq, Hkv, Nq, d, dq_n_slots, kv_n_slots).total;
 }
 
 bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream) {
@@ -251,12 +267,46 @@ bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream)
   if (a->Br != 128 || a->Bc != 64) return fail(BSATTN_ERR_UNSUPPORTED, "the backward needs Br = 128, Bc = 64");
   if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
     return fail(BSATTN_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
-  const size_t need = bsattn_prefill_bwd_workspace_size(a->B, a->Hq, a->Nq);
-  if (a->workspace_bytes < need) return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, need);
+  // schedules: both need the block index; counts consistent with their arrays
+  if (a->dq_items) {
+    if (!a->row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a dQ schedule needs the CSR");
+    if (a->dq_n_items < 1 || a->dq_n_merges < 0 || a->dq_n_slots < a->dq_n_merges || (a->dq_n_merges > 0) != (a->dq_merges != nullptr) ||
+        (a->dq_n_slots > 0) != (a->dq_n_merges > 0))
+      return fail(BSATTN_ERR_INVALID_ARG, "dQ schedule counts inconsistent (items %d, merges %d, slots %d)",
+                  a->dq_n_items, a->dq_n_merges, a->dq_n_slots);
+  } else if (a->dq_n_items || a->dq_n_merges || a->dq_n_slots || a->dq_merges) {
+    return fail(BSATTN_ERR_INVALID_ARG, "dQ schedule counts or merges without items");
+  }
+  if (a->kv_items) {
+    if (!a->col_ptr) return fail(BSATTN_ERR_INVALID_ARG, "a dK/dV schedule needs the CSC");
+    if (a->kv_n_items < 1 || a->kv_n_merges < 0 || a->kv_n_slots < a->kv_n_merges || (a->kv_n_merges > 0) != (a->kv_merges != nullptr) ||
+        (a->kv_n_slots > 0) != (a->kv_n_merges > 0))
+      return fail(BSATTN_ERR_INVALID_ARG, "dK/dV schedule counts inconsistent (items %d, merges %d, slots %d)",
+                  a->kv_n_items, a->kv_n_merges, a->kv_n_slots);
+  } else if (a->kv_n_items || a->kv_n_merges || a->kv_n_slots || a->kv_merges) {
+    return fail(BSATTN_ERR_INVALID_ARG, "dK/dV schedule counts or merges without items");
+  }
+  const int32_t dq_slots = a->dq_items ? a->dq_n_slots : 0, kv_slots = a->kv_items ? a->kv_n_slots : 0;
+  const BwdWorkspace w = bwd_workspace_layout(a->B, a->Hq, a->Hkv, a->Nq, a->d, dq_slots, kv_slots);
+  if (a->workspace_bytes < w.total)
+    return fail(BSATTN_ERR_CAPACITY, "workspace_bytes %zu < required %zu", a->workspace_bytes, w.total);
   BwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.dout = a->dout; p.lse = a->lse;
   p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
-  p.dvec = static_cast<float*>(a->workspace);
+  char* ws = static_cast<char*>(a->workspace);
+  p.dvec = reinterpret_cast<float*>(ws + w.dvec);
+  if (a->dq_items) {
+    p.dq_items = a->dq_items; p.dq_n_items = a->dq_n_items;
+    p.dq_merges = a->dq_merges; p.dq_n_merges = a->dq_n_merges;
+    p.dq_part = reinterpret_cast<float*>(ws + w.dq_part);
+    p.dq_arrive = reinterpret_cast<int32_t*>(ws + w.dq_arrive);
+  }
+  if (a->kv_items) {
+    p.kv_items = a->kv_items; p.kv_n_items = a->kv_n_items;
+    p.kv_merges = a->kv_merges; p.kv_n_merges = a->kv_n_merges;
+    p.kv_part = reinterpret_cast<float*>(ws + w.kv_part);
+    p.kv_arrive = reinterpret_cast<int32_t*>(ws + w.kv_arrive);
+  }
   p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Nk = a->Nk; p.d = a->d;
   p.qs_b = a->q_stride[0]; p.qs_t = a->q_stride[1]; p.qs_h = a->q_stride[2];
   p.ks_b = a->k_stride[0]; p.ks_t = a->k_stride[1]; p.ks_h = a->k_stride[2];
@@ -273,8 +323,8 @@ bsattn_status bsattn_prefill_bwd(const bsattn_prefill_bwd_args* a, void* stream)
   p.Tr = (a->Nq + 127) / 128;
   p.Tc = (a->Nk + 63) / 64;
   p.block_state = a->block_state;
-  if ((int64_t)p.B * p.Hq * p.Tr > 0x7fffffffLL || (int64_t)p.B * p.Hkv * p.Tc > 0x7fffffffLL ||
-      (int64_t)p.B * p.Hq * p.Nq > 0x7fffffffLL)
+  if ((int64_t)p.B * p.Hq * std::max(p.Tr, p.dq_n_items) > 0x7fffffffLL ||
+      (int64_t)p.B * p.Hkv * std::max(p.Tc, p.kv_n_items) > 0x7fffffffLL || (int64_t)p.B * p.Hq * p.Nq > 0x7fffffffLL)
     return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   return hip_status(launch_prefill_bwd(p, stream), "prefill backward launch");
 }

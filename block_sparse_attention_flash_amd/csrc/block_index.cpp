@@ -12,6 +12,7 @@
 // milliseconds for a 66K-token video sequence.
 
 #include <algorithm>
+#include <iterator>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -397,6 +398,66 @@ bsattn_status bsattn_schedule_tile_order(int32_t* items, int32_t n_items) {
     return !cx && x.f[0] < y.f[0];
   });
   std::memcpy(items, it.data(), (size_t)n_items * sizeof(Item));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_build_dkdv_schedule(const int32_t* col_ptr, const int32_t* row_idx, int32_t Tc, int32_t G,
+                                         int32_t d, int32_t max_positions_per_item, int32_t* items,
+                                         int32_t items_capacity, int32_t* merges, int32_t merges_capacity,
+                                         int32_t* n_items, int32_t* n_merges, int32_t* n_slots) {
+  using namespace bsattn;
+  clear_error();
+  if (!col_ptr || !row_idx || Tc < 1 || G < 1 || !n_items || !n_merges || !n_slots)
+    return fail(BSATTN_ERR_INVALID_ARG, "col_ptr / row_idx / counts NULL, Tc < 1 or G < 1");
+  if (d != 64 && d != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", d);
+  if (max_positions_per_item < 1) return fail(BSATTN_ERR_INVALID_ARG, "max_positions_per_item must be >= 1");
+  const int32_t NB = d == 64 ? kDkdvBlocks64 : kDkdvBlocks128;
+  for (int32_t j = 0; j < Tc; ++j) {
+    if (col_ptr[j + 1] < col_ptr[j]) return fail(BSATTN_ERR_INVALID_ARG, "col_ptr decreases at block %d", j);
+    for (int32_t e = col_ptr[j] + 1; e < col_ptr[j + 1]; ++e)
+      if (row_idx[e] <= row_idx[e - 1]) return fail(BSATTN_ERR_INVALID_ARG, "row_idx not ascending for block %d", j);
+  }
+  struct Item { int32_t f[kKvItemInts]; };
+  std::vector<Item> it;
+  std::vector<int32_t> mg;
+  int32_t slots = 0;
+  std::vector<int32_t> uni;
+  for (int32_t m = 0; m * NB < Tc; ++m) {
+    // the tiles of the group: the union of its blocks' ascending lists
+    const int32_t j0 = NB * m, nb = std::min(NB, Tc - j0);
+    const int32_t* l0 = row_idx + col_ptr[j0];
+    const int32_t n0 = col_ptr[j0 + 1] - col_ptr[j0];
+    const int32_t* l1 = nb > 1 ? row_idx + col_ptr[j0 + 1] : nullptr;
+    const int32_t n1 = nb > 1 ? col_ptr[j0 + 2] - col_ptr[j0 + 1] : 0;
+    uni.clear();
+    std::set_union(l0, l0 + n0, l1, l1 + n1, std::back_inserter(uni));
+    const int64_t U = (int64_t)uni.size(), P = (int64_t)G * U;
+    if (P <= max_positions_per_item) {
+      it.push_back({{m, 0, (int32_t)P, 0, 0, 0, -1, -1}});
+      continue;
+    }
+    const int32_t k = (int32_t)((P + max_positions_per_item - 1) / max_positions_per_item);
+    const int32_t mi = (int32_t)(mg.size() / 3);
+    mg.insert(mg.end(), {m, slots, k});
+    for (int32_t c = 0; c < k; ++c) {
+      const int64_t p0 = P * c / k, p1 = P * (c + 1) / k;
+      const int32_t t0 = uni[p0 % U];
+      const int32_t i0 = (int32_t)(std::lower_bound(l0, l0 + n0, t0) - l0);
+      const int32_t i1 = l1 ? (int32_t)(std::lower_bound(l1, l1 + n1, t0) - l1) : 0;
+      it.push_back({{m, (int32_t)p0, (int32_t)p1, (int32_t)(p0 / U), i0, i1, slots + c, mi}});
+    }
+    slots += k;
+  }
+  std::stable_sort(it.begin(), it.end(),
+                   [](const Item& x, const Item& y) { return (x.f[2] - x.f[1]) > (y.f[2] - y.f[1]); });
+  *n_items = (int32_t)it.size();
+  *n_merges = (int32_t)(mg.size() / 3);
+  *n_slots = slots;
+  if (!items) return BSATTN_OK;
+  if (items_capacity < *n_items || (*n_merges > 0 && (!merges || merges_capacity < *n_merges)))
+    return fail(BSATTN_ERR_CAPACITY, "schedule needs %d items and %d merges", *n_items, *n_merges);
+  std::memcpy(items, it.data(), it.size() * sizeof(Item));
+  if (!mg.empty()) std::memcpy(merges, mg.data(), mg.size() * sizeof(int32_t));
   return BSATTN_OK;
 }
 

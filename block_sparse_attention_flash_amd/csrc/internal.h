@@ -83,6 +83,18 @@ struct BwdParams {
   int32_t causal;
   int32_t Tr, Tc;
   const uint8_t* block_state;   // optional [B][Hq][Tr][Tc] of a skipping forward: 2 = no gradient
+  const int32_t* dq_items;      // [dq_n_items][5] schedule of the dQ kernel over the CSR, or NULL
+  int32_t dq_n_items;
+  const int32_t* dq_merges;     // [dq_n_merges][3]
+  int32_t dq_n_merges;
+  float* dq_part;               // [dq_n_slots][B][Hq][128 * d] partial dQ^T in accumulator order
+  int32_t* dq_arrive;           // [dq_n_merges][B][Hq] chunk arrival counters
+  const int32_t* kv_items;      // [kv_n_items][kKvItemInts] schedule of the dK/dV kernel over the CSC, or NULL
+  int32_t kv_n_items;
+  const int32_t* kv_merges;     // [kv_n_merges][3]
+  int32_t kv_n_merges;
+  float* kv_part;               // [kv_n_slots][B][Hkv][blocks per group * 2 * 2 * d * 64] partial dK, dV
+  int32_t* kv_arrive;           // [kv_n_merges][B][Hkv]
 };
 
 int launch_prefill_bwd(const BwdParams& p, void* stream);
@@ -142,6 +154,21 @@ int noalloc_scratch(void** ptr);
 
 // Kernel launchers (HIP translation units).  Return hipError_t as int.
 int launch_prefill_bf16(const PrefillParams& p, void* stream);
+// Key blocks per work-group of the backward dK/dV kernel (they share each
+// query stage's loads): one at d = 64, two at d = 128.
+constexpr int kDkdvBlocks64 = 1;
+constexpr int kDkdvBlocks128 = 2;
+// Ints per item of a dK/dV schedule: {key-block group, first position, end
+// position, head of the first position, list positions of both blocks at
+// the first position, slot, merge}.
+constexpr int kKvItemInts = 8;
+
+struct BwdWorkspace {
+  size_t dvec, dq_part, dq_arrive, kv_part, kv_arrive, total;
+};
+BwdWorkspace bwd_workspace_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t d, int32_t dq_n_slots,
+                                  int32_t kv_n_slots);
+
 // Resident work-groups per CU of the bf16 prefill kernel (its launch bounds).
 constexpr int kPrefillWgPerCu64 = 3;
 constexpr int kPrefillWgPerCu128 = 2;

@@ -29,6 +29,8 @@
 // forward, section 4; its section 3.3 check of the block list before any
 // load applies to both walks here).
 
+#include <cstddef>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -59,49 +61,10 @@ struct BTile {
   __device__ static __forceinline__ int pos(int r, int c) { return (r * CH + (c ^ swz(r))) * 8; }
 };
 
-// A R x D global tile staged through registers: load() issues the global
-// reads of rows [0, nrows) (rows >= nrows read as zeros) one tile ahead,
-// store() writes them to LDS once the tile there is no longer read.
-template <int D, int R>
-struct Staged {
-  static constexpr int CH = D / 8;
-  static constexpr int PER = R * CH / NT;
-  bf16x8 v[PER];
-  __device__ __forceinline__ void load(const __bf16* src, int64_t stride, int nrows, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = i * NT + tid;
-      const int r = x / CH, c = x % CH;
-      v[i] = r < nrows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * stride + 8 * c) : bf16x8{};
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = i * NT + tid;
-      const int r = x / CH, c = x % CH;
-      *reinterpret_cast<bf16x8*>(tile + BTile<D>::pos(r, c)) = v[i];
-    }
-  }
-};
-
 // Row fragment: X[r][16 ks + 8 hi + 0..7] (A operand rows, or B operand columns).
 template <int D>
 __device__ __forceinline__ bf16x8 read_row(const __bf16* tile, int r, int ks, int hi) {
   return *reinterpret_cast<const bf16x8*>(tile + BTile<D>::pos(r, 2 * ks + hi));
-}
-
-// Transposed fragment (A operand X^T[m = d][k]): lane l gets, in slot i,
-// X[r0 + 8 (i/4) + 4 (l/32) + i%4][32 n + l%32], the row order of the
-// accumulator layout above.
-template <int D>
-__device__ __forceinline__ bf16x8 read_tr(const __bf16* tile, int r0, int n, int lane) {
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int r = r0 + 4 * (g16 >> 1) + (j16 >> 2);
-  const int c = 4 * n + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  const int half = 4 * (j16 & 1);
-  return join_bf16x4(lds_read_tr16(tile + BTile<D>::pos(r, c) + half),
-                     lds_read_tr16(tile + BTile<D>::pos(r + 8, c) + half));
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -170,211 +133,60 @@ __device__ __forceinline__ void dma_tile64(__bf16* tile, const __bf16* head, int
   }
 }
 
-template <int D>
-struct DkdvSmem {
-  __bf16 k[BC * D];   // the block's keys
-  __bf16 v[BC * D];
-  __bf16 q[64 * D];   // 64 query rows of the current tile (one stage)
-  __bf16 g[64 * D];   // their dout
-  float lse2[64];     // lse in log2 units
-  float dv[64];
-};
-
-// Work-groups per CU the dK/dV kernel is cut for: K and V stay in LDS and
-// query rows stream in 64-row stages, so two groups fit at d = 128 (64.5 KB
-// of LDS, at most 256 registers each) and three at d = 64.
-template <int D>
-constexpr int kDkdvBlocksPerCu = D == 64 ? 3 : 2;
-
-// One work-group per (batch, K/V head, key block).  Wave w: keys 32 (w & 1)
-// .. +31 of the block (kh), rows 32 (w >> 1) .. +31 of each 64-row stage (qh).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, kDkdvBlocksPerCu<D>) void bwd_dkdv_kernel(const BwdParams p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int KS = D / 16;
-  constexpr int NTD = D / 32;
-  __shared__ DkdvSmem<D> sm;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int kh = wave & 1, qh = wave >> 1;
-  // work order: key block major, ascending (under a causal mask the first
-  // blocks have the most query tiles: longest first); the (batch, K/V head)
-  // index runs fastest, so with B Hkv a multiple of 8 a group stays on one
-  // XCD (work-group i runs on XCD i % 8) and its Q / dO tiles in one L2
-  const int NBG = p.B * p.Hkv;
-  const int j = blockIdx.x / NBG;
-  const int bg = blockIdx.x % NBG;
-  const int g = bg % p.Hkv, b = bg / p.Hkv;
-  const int G = p.Hq / p.Hkv;
-  const float c2 = p.scale * kLog2e;
-
-  const int key = j * BC + 32 * kh + l32;  // this lane's key (column of S)
-  const bool key_ok = key < p.n_valid;
-  dma_tile64<D>(sm.k, static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h, p.Nk, p.ks_t,
-                j * BC, wave, lane);
-  dma_tile64<D>(sm.v, static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h, p.Nk, p.vs_t,
-                j * BC, wave, lane);
-
-  f32x16 dk[NTD], dv[NTD];
-#pragma unroll
-  for (int n = 0; n < NTD; ++n) {
-    dk[n] = f32x16{};
-    dv[n] = f32x16{};
-  }
-
-  // query tiles that attend block j: the transposed CSR, or every tile (from
-  // the diagonal on when causal)
-  int e0, e1;
-  if (p.col_ptr) {
-    e0 = p.col_ptr[j];
-    e1 = p.col_ptr[j + 1];
-  } else {
-    e0 = CAUSAL ? (j * BC) / BR : 0;
-    e1 = p.Tr;
-  }
-  e0 = __builtin_amdgcn_readfirstlane(e0);
-  e1 = __builtin_amdgcn_readfirstlane(e1);
-  const int ntile = e1 - e0;
-
-  // work: (query head, tile, 64-row half) in order; halves past the last row
-  // or (causal) wholly above the block's first key are not visited
-  for (int it = 0; it < 2 * G * ntile; ++it) {
-    const int hf = it & 1;
-    const int e = e0 + (it >> 1) % ntile;
-    const int h = g * G + (it >> 1) / ntile;
-    const int t = __builtin_amdgcn_readfirstlane(p.row_idx ? p.row_idx[e] : e);
-    const int row0 = t * BR + 64 * hf;
-    if (row0 >= p.Nq || (CAUSAL && row0 + 63 < j * BC)) continue;
-    if (p.block_state && p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] == 2) continue;
-    const int nrows = min(64, p.Nq - row0);
-    __syncthreads();  // every wave is done reading the previous stage
-    dma_tile64<D>(sm.q, static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h, p.Nq, p.qs_t,
-                  row0, wave, lane);
-    dma_tile64<D>(sm.g, static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h, p.Nq,
-                  p.dos_t, row0, wave, lane);
-    if (tid < 64) {
-      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + row0 + tid;
-      sm.lse2[tid] = tid < nrows ? p.lse[ri] * kLog2e : 0.0f;
-      sm.dv[tid] = tid < nrows ? p.dvec[ri] : 0.0f;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA has landed
-    __syncthreads();                                   // and every other wave's
-
-    const int r0 = 32 * qh;  // first stage row of this wave's chunk
-    // S = Q K^T and dP = dO V^T, the fragments of one k-step at a time (the
-    // scheduling barriers keep the compiler from hoisting every LDS read,
-    // which would not fit two work-groups' registers)
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(read_row<D>(sm.q, r0 + l32, ks, hi), read_row<D>(sm.k, 32 * kh + l32, ks, hi), s);   // S[q][key]
-      dp = mfma32(read_row<D>(sm.g, r0 + l32, ks, hi), read_row<D>(sm.v, 32 * kh + l32, ks, hi), dp);  // dP[q][key]
-      if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int a = 8 * kk + i;
-        const int rl = r0 + 8 * (a >> 2) + 4 * hi + (a & 3);
-        const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
-        pv[i] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse2[rl])) : 0.0f;
-        dsv[i] = pv[i] * (dp[a] - sm.dv[rl]);
-      }
-      const bf16x8 pb = to_bf16x8(pv);
-      const bf16x8 db = to_bf16x8(dsv);
-#pragma unroll
-      for (int n = 0; n < NTD; ++n) {
-        dv[n] = mfma32(read_tr<D>(sm.g, r0 + 16 * kk, n, lane), pb, dv[n]);  // dV^T += dO^T P
-        dk[n] = mfma32(read_tr<D>(sm.q, r0 + 16 * kk, n, lane), db, dk[n]);  // dK^T += Q^T dS
-        if (n % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  // the two row halves of each key half: waves with qh = 1 hand their sums to
-  // the waves with qh = 0 through LDS (the Q / dO area is free now)
-  __syncthreads();
-  static_assert(sizeof(float) * 2 * 2 * NTD * 16 * 64 <= sizeof(__bf16) * 4 * 64 * D, "reduction fits in k, v, q, g");
-  float* red = reinterpret_cast<float*>(&sm) + kh * (2 * NTD * 16 * 64);
-  if (qh == 1) {
-#pragma unroll
-    for (int n = 0; n < NTD; ++n)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        red[(n * 16 + a) * 64 + lane] = dk[n][a];
-        red[((NTD + n) * 16 + a) * 64 + lane] = dv[n][a];
-      }
-  }
-  __syncthreads();
-  if (qh == 0 && key < p.Nk) {
-    __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
-    __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
-#pragma unroll
-    for (int n = 0; n < NTD; ++n) {
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        dk[n][a] += red[(n * 16 + a) * 64 + lane];
-        dv[n][a] += red[((NTD + n) * 16 + a) * 64 + lane];
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dcol = 32 * n + 8 * q4 + 4 * hi;
-        store4(dkp + dcol, dk[n], q4, p.scale);
-        store4(dvp + dcol, dv[n], q4, 1.0f);
-      }
-    }
-  }
-#endif
-}
-
-// ---- dK/dV at d = 128: key-block pairs, double-buffered query stages --------
+// ---- dK/dV: double-buffered query stages ------------------------------------
 //
-// The kernel above keeps one 64-row query stage in LDS and waits for each
-// stage's load before computing on it: at d = 128 two work-groups fill a
-// CU's LDS, so the load latency of every stage is exposed to the MFMAs of
-// only one other work-group.  Here one work-group of eight waves takes two
-// adjacent key blocks (2m, 2m + 1), so their K/V (64 KB) and two 64-row
-// query stages (64 KB) fit one CU: the next stage streams in while the
-// current one is computed, behind a single barrier per stage.  Waves 4 kb ..
-// 4 kb + 3 work on block 2m + kb exactly as the four waves above do; the
-// stages visited are those of either block (the union of the two tiles'
-// lists, or the shared causal range), and a block's waves sit out stages that
-// do not touch it.  The Q / dO stages' transposed reads are inline asm that
-// waits inside the block: the intrinsic would make the compiler wait for
-// the next stage's load first (it cannot tell the stages apart).
-
-constexpr int NT2 = 512;
+// One work-group per (batch, K/V head, group of NB adjacent key blocks).  K
+// and V of its blocks stay in LDS; the query rows of every tile that attends
+// one of them stream in 64-row stages (Q, dO, and the rows' lse and Dv),
+// double-buffered: the next stage lands while the current one is computed,
+// behind a single barrier per stage.  Waves 4 kb .. 4 kb + 3 work on block
+// NB m + kb: wave bits (kh, qh) pick keys 32 kh .. +31 of the block and rows
+// 32 qh .. +31 of the stage.  The stages visited are those of any of the
+// blocks (the union of their tiles' lists, or the shared causal range), and
+// a block's waves sit out stages that do not touch it.
+//
+// At d = 128, NB = 2: two blocks share each stage's loads, one work-group of
+// eight waves per CU (129 KB of LDS).  At d = 64, NB = 1: three four-wave
+// work-groups per CU (49 KB each); pairs there (one or two eight-wave groups
+// per CU) measured slower on the multimodal DiT shape, which has few key
+// blocks per head.  The stages' transposed reads are inline asm that waits
+// inside the block: the intrinsic would make the compiler wait for the next
+// stage's load first (it cannot tell the stages apart).
 
 template <int D>
-struct Dkdv2Smem {
-  __bf16 k[2][BC * D];  // keys of blocks 2m, 2m + 1
-  __bf16 v[2][BC * D];
+constexpr int kDkdvBlocks = D == 64 ? kDkdvBlocks64 : kDkdvBlocks128;
+template <int D>
+constexpr int kDkdvGroupsPerCu = D == 64 ? 3 : 1;
+
+template <int D, int NB>
+struct DkdvSmem {
+  __bf16 k[NB][BC * D];  // keys of blocks NB m .. NB m + NB - 1
+  __bf16 v[NB][BC * D];
   __bf16 q[2][64 * D];  // double-buffered 64-row query stages
   __bf16 g[2][64 * D];  // their dout
   float lse[2][64];     // per stage: lse (natural log) and Dv of its rows
   float dvec[2][64];
+  int ticket;           // a chunk's arrival ticket (after the reduction, which overlays the tiles)
 };
 
-// 64 x D tile, global -> LDS, by all eight waves (rows past rows_total: zeros).
-template <int D>
-__device__ __forceinline__ void dma_tile64_w8(__bf16* tile, const __bf16* head, int rows_total, int64_t stride_t,
+// 64 x D tile, global -> LDS, by all NW waves of the work-group (rows past
+// rows_total: zeros); the layout of dma_tile64 for any wave count.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile64_wn(__bf16* tile, const __bf16* head, int rows_total, int64_t stride_t,
                                               int row0, int wave, int lane) {
   constexpr int CH = D / 8;
-  constexpr int NI = 64 * CH / NT2;
+  constexpr int NI = 64 * CH / (64 * NW);
   const uint32_t extent = (uint32_t)(((int64_t)(rows_total - 1) * stride_t + D) * 2);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, (int)extent, kBufferWord3);
   const uint32_t soff = (uint32_t)((int64_t)row0 * stride_t * 2);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int slot = (8 * i + wave) * 64 + lane;
+    const int slot = (NW * i + wave) * 64 + lane;
     const int r = slot / CH, cp = slot % CH;
     const int c = cp ^ BTile<D>::swz(r);
     const uint32_t voff = (uint32_t)(((int64_t)r * stride_t + 8 * c) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (8 * i + wave) * 64 * 8), 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (NW * i + wave) * 64 * 8), 16, voff, soff, 0, 0);
   }
 }
 
@@ -387,79 +199,127 @@ __device__ __forceinline__ void dma_row64(float* dst, const float* src_row, int 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, (uint32_t)lane * 4, (uint32_t)row0 * 4, 0, 0);
 }
 
-// The four d-tiles' transposed fragments of one 16-row step (read_tr for
-// n = 0..3), issued together and waited for inside the asm block.  The
-// loads return into their registers some cycles after the block issues
+// Transposed fragments (A operands X^T[m = d][k]) of one 16-row step at row
+// r0, for the D / 32 d-tiles n: lane l gets, in slot i of out[n],
+// X[r0 + 8 (i/4) + 4 (l/32) + i%4][32 n + l%32], the row order of the
+// accumulator layout above.  The loads are issued together and waited for
+// inside the asm block.
+// The loads return into their registers some cycles after the block issues
 // them, which the compiler does not see: `busy` (the operands of the MFMAs
-// issued just before, which may not have read them yet) are inputs of the
-// block, so its outputs (early-clobber) are never placed on top of them.
-__device__ __forceinline__ void read_tr_x4(bf16x8 (&out)[4], const __bf16* tile, int r0, int lane,
-                                           const bf16x8 (&busy)[4], const bf16x8& busy_b) {
+// issued just before) are inputs of the block, and its outputs are
+// early-clobber, so no output is placed on an input.
+template <int D>
+__device__ __forceinline__ void read_tr_xn(bf16x8 (&out)[D / 32], const __bf16* tile, int r0, int lane,
+                                           const bf16x8 (&busy)[D / 32], const bf16x8& busy_b) {
+  constexpr int NN = D / 32;
   const int g16 = lane >> 4, j16 = lane & 15;
   const int r = r0 + 4 * (g16 >> 1) + (j16 >> 2);
   const int half = 4 * (j16 & 1);
-  uint32_t a[8];
+  uint32_t a[2 * NN];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
+  for (int n = 0; n < NN; ++n) {
     const int c = 4 * n + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-    a[2 * n] = lds_addr_b(tile + BTile<128>::pos(r, c) + half);
-    a[2 * n + 1] = lds_addr_b(tile + BTile<128>::pos(r + 8, c) + half);
+    a[2 * n] = lds_addr_b(tile + BTile<D>::pos(r, c) + half);
+    a[2 * n + 1] = lds_addr_b(tile + BTile<D>::pos(r + 8, c) + half);
   }
-  i16x4 x[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %9\n"
-      "ds_read_b64_tr_b16 %2, %10\n"
-      "ds_read_b64_tr_b16 %3, %11\n"
-      "ds_read_b64_tr_b16 %4, %12\n"
-      "ds_read_b64_tr_b16 %5, %13\n"
-      "ds_read_b64_tr_b16 %6, %14\n"
-      "ds_read_b64_tr_b16 %7, %15\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(busy[0]),
-        "v"(busy[1]), "v"(busy[2]), "v"(busy[3]), "v"(busy_b)
-      : "memory");
+  i16x4 x[2 * NN];
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %9\n"
+        "ds_read_b64_tr_b16 %2, %10\n"
+        "ds_read_b64_tr_b16 %3, %11\n"
+        "ds_read_b64_tr_b16 %4, %12\n"
+        "ds_read_b64_tr_b16 %5, %13\n"
+        "ds_read_b64_tr_b16 %6, %14\n"
+        "ds_read_b64_tr_b16 %7, %15\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(busy[0]),
+          "v"(busy[1]), "v"(busy[2]), "v"(busy[3]), "v"(busy_b)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n"
+        "ds_read_b64_tr_b16 %1, %5\n"
+        "ds_read_b64_tr_b16 %2, %6\n"
+        "ds_read_b64_tr_b16 %3, %7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(busy[0]), "v"(busy[1]), "v"(busy_b)
+        : "memory");
+  }
 #pragma unroll
-  for (int n = 0; n < 4; ++n) out[n] = join_bf16x4(x[2 * n], x[2 * n + 1]);
+  for (int n = 0; n < NN; ++n) out[n] = join_bf16x4(x[2 * n], x[2 * n + 1]);
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p) {
+// launch bound: waves per SIMD (a work-group puts NB waves on each SIMD)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsPerCu<D>) void bwd_dkdv_kernel(
+    const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int D = 128;
+  constexpr int NB = kDkdvBlocks<D>;
+  constexpr int NW = 4 * NB;
   constexpr int KS = D / 16;
   constexpr int NTD = D / 32;
-  __shared__ Dkdv2Smem<D> sm;
+  __shared__ DkdvSmem<D, NB> sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int kb = wave >> 2, kh = wave & 1, qh = (wave >> 1) & 1;
-  // work order as above: key-block pairs ascending, (batch, K/V head) fastest
+  // work order: key-block groups ascending (under a causal mask the first
+  // blocks have the most query tiles: longest first), or the schedule's
+  // items (longest first); the (batch, K/V head) index runs fastest, so with
+  // B Hkv a multiple of 8 a group stays on one XCD (work-group i runs on XCD
+  // i % 8) and its Q / dO tiles in one L2
   const int NBG = p.B * p.Hkv;
-  const int m = blockIdx.x / NBG;
+  const int rank = blockIdx.x / NBG;
   const int bg = blockIdx.x % NBG;
+  // the item: a group's (query head, tile) positions [pos_begin, pos_end)
+  // in head-major order, starting at head hc0 with list positions (i00, i10)
+  int m = rank, pos_begin = 0, pos_end = INT32_MAX, hc0 = 0, i00 = 0, i10 = 0, slot = -1, mrg = -1;
+  if (p.kv_items) {
+    const int32_t* item = p.kv_items + kKvItemInts * rank;
+    m = item[0];
+    pos_begin = item[1];
+    pos_end = item[2];
+    hc0 = item[3];
+    i00 = item[4];
+    i10 = item[5];
+    slot = item[6];
+    mrg = item[7];
+  }
+  m = __builtin_amdgcn_readfirstlane(m);
+  pos_begin = __builtin_amdgcn_readfirstlane(pos_begin);
+  pos_end = __builtin_amdgcn_readfirstlane(pos_end);
+  hc0 = __builtin_amdgcn_readfirstlane(hc0);
+  i00 = __builtin_amdgcn_readfirstlane(i00);
+  i10 = __builtin_amdgcn_readfirstlane(i10);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  mrg = __builtin_amdgcn_readfirstlane(mrg);
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const int G = p.Hq / p.Hkv;
   const float c2 = p.scale * kLog2e;
-  const int j0 = 2 * m;
-  const bool has1 = j0 + 1 < p.Tc;
+  const int j0 = NB * m;
+  const bool has1 = NB == 2 && j0 + 1 < p.Tc;
   const int jw = j0 + kb;  // this wave's block
 
   const int key = jw * BC + 32 * kh + l32;
   const bool key_ok = key < p.n_valid;
   const __bf16* kh_base = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
   const __bf16* vh_base = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
-  dma_tile64_w8<D>(sm.k[0], kh_base, p.Nk, p.ks_t, j0 * BC, wave, lane);
-  dma_tile64_w8<D>(sm.v[0], vh_base, p.Nk, p.vs_t, j0 * BC, wave, lane);
-  if (has1) {
-    dma_tile64_w8<D>(sm.k[1], kh_base, p.Nk, p.ks_t, (j0 + 1) * BC, wave, lane);
-    dma_tile64_w8<D>(sm.v[1], vh_base, p.Nk, p.vs_t, (j0 + 1) * BC, wave, lane);
+  dma_tile64_wn<D, NW>(sm.k[0], kh_base, p.Nk, p.ks_t, j0 * BC, wave, lane);
+  dma_tile64_wn<D, NW>(sm.v[0], vh_base, p.Nk, p.vs_t, j0 * BC, wave, lane);
+  if constexpr (NB == 2) {
+    if (has1) {
+      dma_tile64_wn<D, NW>(sm.k[1], kh_base, p.Nk, p.ks_t, (j0 + 1) * BC, wave, lane);
+      dma_tile64_wn<D, NW>(sm.v[1], vh_base, p.Nk, p.vs_t, (j0 + 1) * BC, wave, lane);
+    }
   }
 
   // the stages: for each query head of the group, the tiles holding either
   // block (merge of the two transposed lists, or the causal / dense range
-  // shared by the pair), two 64-row halves each; a stage is kept when it
+  // shared by the group), two 64-row halves each; a stage is kept when it
   // touches a block (not past the last row, not wholly above the block's
   // first key, not a block the forward skipped for that head and tile)
   // the transposed index through the scalar cache (wave-uniform, read-only)
@@ -474,15 +334,16 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
       n1 = p.col_ptr[j0 + 2] - b1;
     }
   } else {
-    tlo = CAUSAL ? (j0 * BC) / BR : 0;  // both blocks of the pair start at this tile
+    tlo = CAUSAL ? (j0 * BC) / BR : 0;  // every block of the group starts at this tile
   }
   b0 = __builtin_amdgcn_readfirstlane(b0);
   n0 = __builtin_amdgcn_readfirstlane(n0);
   b1 = __builtin_amdgcn_readfirstlane(b1);
   n1 = __builtin_amdgcn_readfirstlane(n1);
-  // cursor: head index hc, list positions (i0, i1) or tile tc, half hf
+  // cursor: head index hc, list positions (i0, i1) or tile tc, half hf, and
+  // the position (head, tile) index
   struct Cur {
-    int hc, i0, i1, tc, hf;
+    int hc, i0, i1, tc, hf, pos;
   };
   auto touches = [&](int h, int t, int hf, int jb) __attribute__((always_inline)) {
     const int row0 = t * BR + 64 * hf;
@@ -512,6 +373,7 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
       return;
     }
     c.hf = 0;
+    ++c.pos;
     if (p.col_ptr) {
       tile_at(c, in0, in1);
       c.i0 += in0 ? 1 : 0;
@@ -523,11 +385,11 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
   // advance c to the first kept stage at or after it; false when none is left
   auto settle = [&](Cur& c, int& t, int& need) __attribute__((always_inline)) {
     for (;;) {
-      if (c.hc >= G) return false;
+      if (c.hc >= G || c.pos >= pos_end) return false;
       bool in0, in1;
       t = tile_at(c, in0, in1);
-      if (t < 0) {  // next head
-        c = Cur{c.hc + 1, 0, 0, tlo, 0};
+      if (t < 0) {  // next head (a head's positions end with its last tile)
+        c = Cur{c.hc + 1, 0, 0, tlo, 0, c.pos};
         continue;
       }
       const int h = g * G + c.hc;
@@ -538,10 +400,10 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
   };
   auto fetch = [&](int buf, int h, int t, int hf) __attribute__((always_inline)) {
     const int row0 = t * BR + 64 * hf;
-    dma_tile64_w8<D>(sm.q[buf], static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h, p.Nq,
-                     p.qs_t, row0, wave, lane);
-    dma_tile64_w8<D>(sm.g[buf], static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h,
-                     p.Nq, p.dos_t, row0, wave, lane);
+    dma_tile64_wn<D, NW>(sm.q[buf], static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h,
+                         p.Nq, p.qs_t, row0, wave, lane);
+    dma_tile64_wn<D, NW>(sm.g[buf], static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h,
+                         p.Nq, p.dos_t, row0, wave, lane);
     const int64_t rb = ((int64_t)b * p.Hq + h) * p.Nq;
     if (wave == 0) dma_row64(sm.lse[buf], p.lse + rb, p.Nq, row0, lane);
     if (wave == 1) dma_row64(sm.dvec[buf], p.dvec + rb, p.Nq, row0, lane);
@@ -554,7 +416,7 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
     dv[n] = f32x16{};
   }
 
-  Cur cur{0, 0, 0, tlo, 0};
+  Cur cur{hc0, i00, i10, tlo, 0, pos_begin};
   int t_cur = 0, need_cur = 0;
   bool have = settle(cur, t_cur, need_cur);
   if (have) fetch(0, g * G + cur.hc, t_cur, cur.hf);
@@ -563,7 +425,7 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
     // this stage (and, the first time, K and V) has landed in every wave, and
     // every wave is done with the previous stage, whose buffers are next
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const int h = g * G + cur.hc, t = t_cur, hf = cur.hf, need = need_cur;
+    const int t = t_cur, hf = cur.hf, need = need_cur;
     Cur nxt = cur;
     step(nxt);
     int t_nxt = 0, need_nxt = 0;
@@ -577,9 +439,9 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
       const __bf16* sq = sm.q[buf];
       const __bf16* sg = sm.g[buf];
       f32x16 s = f32x16{}, dp = f32x16{};
-      bf16x8 frg[4], frq[4], dbp = bf16x8{};
+      bf16x8 frg[NTD], frq[NTD], dbp = bf16x8{};
 #pragma unroll
-      for (int n = 0; n < 4; ++n) frq[n] = bf16x8{};
+      for (int n = 0; n < NTD; ++n) frq[n] = bf16x8{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32(read_row<D>(sq, r0 + l32, ks, hi), read_row<D>(sm.k[kb], 32 * kh + l32, ks, hi), s);
@@ -601,10 +463,10 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
         const bf16x8 db = to_bf16x8(dsv);
         // (the first read follows the dK products of the previous step; the
         // S and dP products before the first step have been waited for)
-        read_tr_x4(frg, sg, r0 + 16 * kk, lane, frq, dbp);
+        read_tr_xn<D>(frg, sg, r0 + 16 * kk, lane, frq, dbp);
 #pragma unroll
         for (int n = 0; n < NTD; ++n) dv[n] = mfma32(frg[n], pb, dv[n]);  // dV^T += dO^T P
-        read_tr_x4(frq, sq, r0 + 16 * kk, lane, frg, pb);
+        read_tr_xn<D>(frq, sq, r0 + 16 * kk, lane, frg, pb);
 #pragma unroll
         for (int n = 0; n < NTD; ++n) dk[n] = mfma32(frq[n], db, dk[n]);  // dK^T += Q^T dS
         dbp = db;
@@ -620,7 +482,9 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
   // with qh = 0 through LDS (free once every wave is past its last stage)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  static_assert(sizeof(float) * 4 * 2 * NTD * 16 * 64 <= sizeof(Dkdv2Smem<D>), "reduction fits in the tiles");
+  using Sm = DkdvSmem<D, NB>;
+  static_assert(sizeof(float) * 2 * NB * 2 * NTD * 16 * 64 <= offsetof(Sm, ticket),
+                "reduction fits in the tiles, clear of the ticket");
   float* red = reinterpret_cast<float*>(&sm) + (2 * kb + kh) * (2 * NTD * 16 * 64);
   if (qh == 1) {
 #pragma unroll
@@ -632,16 +496,64 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
       }
   }
   __syncthreads();
-  if (qh == 0 && jw < p.Tc && key < p.Nk) {
-    __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
-    __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
+  if (qh == 0) {
 #pragma unroll
-    for (int n = 0; n < NTD; ++n) {
+    for (int n = 0; n < NTD; ++n)
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         dk[n][a] += red[(n * 16 + a) * 64 + lane];
         dv[n][a] += red[((NTD + n) * 16 + a) * 64 + lane];
       }
+  }
+  if (slot >= 0) {
+    // ---- chunk of a cut group: the waves holding the sums (qh = 0) publish
+    //      them, the work-group takes an arrival ticket, and the last chunk
+    //      to arrive adds every partial of the group in slot order (its own
+    //      read back like the others)
+    constexpr int PER = NB * 2 * 2 * NTD * 16 * 64;  // floats per (slot, batch, K/V head)
+    const int s0 = p.kv_merges[3 * mrg + 1];
+    const int ns = p.kv_merges[3 * mrg + 2];
+    auto part = [&](int sl) __attribute__((always_inline)) {
+      return p.kv_part + (((int64_t)sl * p.B + b) * p.Hkv + g) * PER + (2 * kb + kh) * (2 * NTD * 16 * 64) + lane;
+    };
+    if (qh == 0) {
+      float* pp = part(slot);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          store_coherent(pp + (n * 16 + a) * 64, dk[n][a]);
+          store_coherent(pp + ((NTD + n) * 16 + a) * 64, dv[n][a]);
+        }
+    }
+    wait_stores_done();
+    __syncthreads();  // every wave's partial has completed
+    if (tid == 0) sm.ticket = atomicAdd(p.kv_arrive + ((int64_t)mrg * p.B + b) * p.Hkv + g, 1);
+    __syncthreads();
+    if (sm.ticket != ns - 1) return;  // a later chunk adds them up
+    if (qh == 0) {
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) {
+        dk[n] = f32x16{};
+        dv[n] = f32x16{};
+      }
+      for (int sl = s0; sl < s0 + ns; ++sl) {
+        const float* pp = part(sl);
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) {
+            dk[n][a] += load_coherent(pp + (n * 16 + a) * 64);
+            dv[n][a] += load_coherent(pp + ((NTD + n) * 16 + a) * 64);
+          }
+      }
+    }
+  }
+  if (qh == 0 && jw < p.Tc && key < p.Nk) {
+    __bf16* dkp = static_cast<__bf16*>(p.dk) + (int64_t)b * p.dks_b + (int64_t)key * p.dks_t + (int64_t)g * p.dks_h;
+    __bf16* dvp = static_cast<__bf16*>(p.dv) + (int64_t)b * p.dvs_b + (int64_t)key * p.dvs_t + (int64_t)g * p.dvs_h;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int dcol = 32 * n + 8 * q4 + 4 * hi;
@@ -653,24 +565,32 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_pair_kernel(const BwdParams p
 #endif
 }
 
+// dQ: one work-group per (batch, query head, query tile or chunk of its CSR
+// list); wave w owns rows 32 w .. 32 w + 31 of the tile, one row per lane
+// (split over l and l + 32).  Per visited key block
+//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - Dv), dQ^T += K^T dS^T
+// with Q and dO in registers and the key blocks streamed global -> LDS by
+// DMA into two stages: block e + 1 lands while block e is computed, behind
+// one barrier per block.  (At d = 64 a form that staged the next block
+// through registers measured 3 % faster without a schedule on the
+// multimodal DiT shape; one kernel serves both head dims.)  The transposed
+// reads are asm blocks under the same rule as in the dK/dV kernel.
 template <int D>
-struct DqSmem {
-  __bf16 k[BC * D];
-  __bf16 v[BC * D];
-};
+constexpr int kDqBlocksPerCu = D == 64 ? 3 : 2;
 
-// One work-group per (batch, query head, query tile); wave w owns rows
-// 32 w .. 32 w + 31 of the tile, one row per lane (split over l and l + 32).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 16;
   constexpr int NTD = D / 32;
-  __shared__ DqSmem<D> sm;
+  __shared__ __bf16 smk[2][BC * D];
+  __shared__ __bf16 smv[2][BC * D];
+  __shared__ int ticket;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  // work order: tile major (under a causal mask the last tiles, the longest,
+  // work order: rank major (tiles, or the schedule's items, longest first;
+  // under a causal mask without a schedule the last tiles, the longest,
   // first), then the group's query heads, the (batch, K/V head) index
   // fastest: with B Hkv a multiple of 8 a group stays on one XCD
   const int G = p.Hq / p.Hkv;
@@ -678,123 +598,26 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdParams p) {
   const int bg = blockIdx.x % NBG;
   const int hh = (blockIdx.x / NBG) % G;
   const int rank = blockIdx.x / (NBG * G);
-  const int t = CAUSAL ? p.Tr - 1 - rank : rank;
-  const int g = bg % p.Hkv, b = bg / p.Hkv;
-  const int h = g * G + hh;
-  const float c2 = p.scale * kLog2e;
-
-  const int row = t * BR + wave * 32 + l32;
-  const bool row_ok = row < p.Nq;
-  const __bf16* qrow = static_cast<const __bf16*>(p.q) + (int64_t)b * p.qs_b + (int64_t)row * p.qs_t + (int64_t)h * p.qs_h;
-  const __bf16* grow =
-      static_cast<const __bf16*>(p.dout) + (int64_t)b * p.dos_b + (int64_t)row * p.dos_t + (int64_t)h * p.dos_h;
-  bf16x8 qf[KS], gf[KS];  // B operands: X[row][16 ks + 8 hi + 0..7]
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hi) : bf16x8{};
-    gf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(grow + 16 * ks + 8 * hi) : bf16x8{};
-  }
-  const int64_t ri = ((int64_t)b * p.Hq + h) * p.Nq + row;
-  const float lse2 = row_ok ? p.lse[ri] * kLog2e : 0.0f;
-  const float dvr = row_ok ? p.dvec[ri] : 0.0f;
-
-  // visited blocks: the tile's CSR list (or every block), minus blocks wholly
-  // above the diagonal, exactly as the forward visits them
-  const int last_row = min(t * BR + BR, p.Nq) - 1;
-  int e0 = p.row_ptr ? p.row_ptr[t] : 0;
-  int e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
-  if (CAUSAL) {
+  int t, e0, e1, slot = -1, mrg = -1;
+  if (p.dq_items) {  // a work item of the schedule: a tile, or a chunk of its CSR list
+    const int32_t* item = p.dq_items + 5 * rank;
+    t = item[0];
+    e0 = item[1];
+    e1 = item[2];
+    slot = item[3];
+    mrg = item[4];
+  } else {
+    t = CAUSAL ? p.Tr - 1 - rank : rank;
+    e0 = 0;
+    e1 = p.Tc;
     if (p.row_ptr) {
-      while (e1 > e0 && p.col_idx[e1 - 1] * BC > last_row) --e1;
-    } else {
-      e1 = min(e1, last_row / BC + 1);
+      e0 = p.row_ptr[t];
+      e1 = p.row_ptr[t + 1];
     }
   }
-  e0 = __builtin_amdgcn_readfirstlane(e0);
-  e1 = __builtin_amdgcn_readfirstlane(e1);
-
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
-  f32x16 dq[NTD];
-#pragma unroll
-  for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
-
-  // the next block's K and V are read into registers while this one computes
-  Staged<D, BC> nk, nv;
-  auto fetch = [&](int e) __attribute__((always_inline)) {
-    const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
-    const int nkeys = min(BC, p.Nk - j * BC);
-    nk.load(kbase + (int64_t)(j * BC) * p.ks_t, p.ks_t, nkeys, tid);
-    nv.load(vbase + (int64_t)(j * BC) * p.vs_t, p.vs_t, nkeys, tid);
-  };
-  if (e0 < e1) fetch(e0);
-  const uint8_t* skipped = p.block_state ? p.block_state + (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc : nullptr;
-  for (int e = e0; e < e1; ++e) {
-    const int j = __builtin_amdgcn_readfirstlane(p.row_ptr ? p.col_idx[e] : e);
-    __syncthreads();  // every wave is done reading the previous block
-    nk.store(sm.k, tid);
-    nv.store(sm.v, tid);
-    __syncthreads();
-    if (e + 1 < e1) fetch(e + 1);
-    if (skipped && skipped[j] == 2) continue;  // the forward skipped it: no gradient (uniform branch)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row<D>(sm.k, 32 * mt + l32, ks, hi), qf[ks], s);   // S^T[key][q]
-        dp = mfma32(read_row<D>(sm.v, 32 * mt + l32, ks, hi), gf[ks], dp);  // dP^T[key][q]
-      }
-      float dsv[16];
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int key = j * BC + 32 * mt + 8 * (a >> 2) + 4 * hi + (a & 3);
-        const bool ok = row_ok && key < p.n_valid && (!CAUSAL || key <= row);
-        const float pr = ok ? fast_exp2(fmaf(s[a], c2, -lse2)) : 0.0f;
-        dsv[a] = pr * (dp[a] - dvr);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 db = to_bf16x8(dsv + 8 * kk);
-#pragma unroll
-        for (int n = 0; n < NTD; ++n) dq[n] = mfma32(read_tr<D>(sm.k, 32 * mt + 16 * kk, n, lane), db, dq[n]);
-      }
-    }
-  }
-
-  if (row_ok) {
-    __bf16* dqp = static_cast<__bf16*>(p.dq) + (int64_t)b * p.dqs_b + (int64_t)row * p.dqs_t + (int64_t)h * p.dqs_h;
-#pragma unroll
-    for (int n = 0; n < NTD; ++n)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) store4(dqp + 32 * n + 8 * q4 + 4 * hi, dq[n], q4, p.scale);
-  }
-#endif
-}
-
-// dQ at d = 128 with the key blocks streamed global -> LDS by DMA into two
-// stages (the kernel above reads the next block into registers and copies
-// it to LDS between two barriers): block e + 1 lands while block e is
-// computed, behind one barrier per block.  The transposed reads are asm
-// blocks under the same rule as in the dK/dV pair kernel.
-template <bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int D = 128;
-  constexpr int KS = D / 16;
-  constexpr int NTD = D / 32;
-  __shared__ __bf16 smk[2][BC * D];
-  __shared__ __bf16 smv[2][BC * D];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  // work order as above
-  const int G = p.Hq / p.Hkv;
-  const int NBG = p.B * p.Hkv;
-  const int bg = blockIdx.x % NBG;
-  const int hh = (blockIdx.x / NBG) % G;
-  const int rank = blockIdx.x / (NBG * G);
-  const int t = CAUSAL ? p.Tr - 1 - rank : rank;
+  t = __builtin_amdgcn_readfirstlane(t);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  mrg = __builtin_amdgcn_readfirstlane(mrg);
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const int h = g * G + hh;
   const float c2 = p.scale * kLog2e;
@@ -814,9 +637,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
   const float lse2 = row_ok ? p.lse[ri] * kLog2e : 0.0f;
   const float dvr = row_ok ? p.dvec[ri] : 0.0f;
 
+  // visited blocks: the item's CSR range (or every block), minus blocks
+  // wholly above the diagonal, exactly as the forward visits them
   const int last_row = min(t * BR + BR, p.Nq) - 1;
-  int e0 = p.row_ptr ? p.row_ptr[t] : 0;
-  int e1 = p.row_ptr ? p.row_ptr[t + 1] : p.Tc;
   if (CAUSAL) {
     if (p.row_ptr) {
       while (e1 > e0 && p.col_idx[e1 - 1] * BC > last_row) --e1;
@@ -844,9 +667,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
   const uint8_t* skipped = p.block_state ? p.block_state + (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc : nullptr;
   int j = blk(e0), jn = blk(e0 + 1);
   if (e0 < e1) fetch(0, j);
-  bf16x8 fa[4], fb[4], dbp = bf16x8{};
+  bf16x8 fa[NTD], fb[NTD], dbp = bf16x8{};
 #pragma unroll
-  for (int n = 0; n < 4; ++n) fb[n] = bf16x8{};
+  for (int n = 0; n < NTD; ++n) fb[n] = bf16x8{};
   for (int e = e0; e < e1; ++e) {
     const int buf = (e - e0) & 1;
     // block e has landed in every wave, and every wave is done with block e - 1
@@ -875,16 +698,49 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
         dsv[a] = pr * (dp[a] - dvr);
       }
       const bf16x8 d0 = to_bf16x8(dsv), d1 = to_bf16x8(dsv + 8);
-      read_tr_x4(fa, sk, 32 * mt, lane, fb, dbp);
+      read_tr_xn<D>(fa, sk, 32 * mt, lane, fb, dbp);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fa[n], d0, dq[n]);
-      read_tr_x4(fb, sk, 32 * mt + 16, lane, fa, d0);
+      read_tr_xn<D>(fb, sk, 32 * mt + 16, lane, fa, d0);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fb[n], d1, dq[n]);
       dbp = d1;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (slot >= 0) {
+    // ---- chunk of a cut tile: publish the partial dQ^T (accumulator order,
+    //      element 16 n + a of thread tid at [16 n + a][tid]), take an
+    //      arrival ticket; the last chunk to arrive adds every partial of the
+    //      tile in slot order (its own read back like the others)
+    const int s0 = p.dq_merges[3 * mrg + 1];
+    const int ns = p.dq_merges[3 * mrg + 2];
+    auto part = [&](int sl) __attribute__((always_inline)) {
+      return p.dq_part + (((int64_t)sl * p.B + b) * p.Hq + h) * BR * D + tid;
+    };
+    {
+      float* po = part(slot);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) store_coherent(po + (16 * n + a) * NT, dq[n][a]);
+    }
+    wait_stores_done();
+    __syncthreads();  // every wave's partial has completed
+    if (tid == 0) ticket = atomicAdd(p.dq_arrive + ((int64_t)mrg * p.B + b) * p.Hq + h, 1);
+    __syncthreads();
+    if (ticket != ns - 1) return;  // a later chunk adds them up
+#pragma unroll
+    for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
+    for (int sl = s0; sl < s0 + ns; ++sl) {
+      const float* po = part(sl);
+#pragma unroll
+      for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) dq[n][a] += load_coherent(po + (16 * n + a) * NT);
+    }
+  }
 
   if (row_ok) {
     __bf16* dqp = static_cast<__bf16*>(p.dq) + (int64_t)b * p.dqs_b + (int64_t)row * p.dqs_t + (int64_t)h * p.dqs_h;
@@ -896,6 +752,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_db_kernel(const BwdParams p) {
 #endif
 }
 
+// Zero n words (the chunk arrival counters of the schedules).
+__global__ __launch_bounds__(NT) void bwd_clear_kernel(int32_t* w, int n) {
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) w[i] = 0;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
@@ -903,16 +764,23 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)dot_blocks), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * ((p.Tc + 1) / 2))),
-                       dim3(NT2), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * p.Tc)), dim3(NT), 0, s, p);
+  // the arrival counters sit at offsets that depend on the call's shape, so
+  // a shared workspace may hold any bytes there: zero them first
+  const struct { int32_t* w; int n; } clears[] = {{p.dq_arrive, p.dq_n_merges * p.B * p.Hq},
+                                                  {p.kv_arrive, p.kv_n_merges * p.B * p.Hkv}};
+  for (const auto& c : clears) {
+    if (!c.w || c.n == 0) continue;
+    hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)min(64, (c.n + NT - 1) / NT)), dim3(NT), 0, s, c.w, c.n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  constexpr int NB = kDkdvBlocks<D>;
+  const int64_t kv_units = p.kv_items ? p.kv_n_items : (p.Tc + NB - 1) / NB;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * kv_units)), dim3(256 * NB),
+                     0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dq_db_kernel<CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Tr)), dim3(NT), 0, s, p);
+  const int64_t dq_units = p.dq_items ? p.dq_n_items : p.Tr;
+  hipLaunchKernelGGL((bwd_dq_db_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hq * dq_units)), dim3(NT), 0, s,
+                     p);
   return hipGetLastError();
 }
 

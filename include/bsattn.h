@@ -299,10 +299,18 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
  * block-sparse forward, section 4).  Every element of dq, dk, dv (rows < Nq,
  * keys < Nk) is written; keys or rows that attend nothing get zeros.
  *
- * Three launches on `stream`: rowsum(dout * out) into the workspace, dk/dv
- * (one work-group per batch, K/V head and 64-key block, walking the CSC over
- * the group's query heads), dq (one work-group per batch, head and 128-row
- * tile, walking the CSR).  No atomics: results are deterministic.
+ * Launches on `stream`: rowsum(dout * out) into the workspace, dk/dv (one
+ * work-group per batch, K/V head and group of adjacent 64-key blocks - one
+ * block at d = 64, two at d = 128 - walking the CSC over the group's query
+ * heads), dq (one work-group per batch, head and 128-row tile, walking the
+ * CSR).  Optional schedules cut long work items (DiT article section 5.3:
+ * uneven rows unbalance the GPU): dq_items from bsattn_build_schedule on the
+ * CSR, kv_items from bsattn_build_dkdv_schedule on the CSC.  A chunk writes
+ * fp32 partial sums to the workspace; the last chunk of an item to arrive
+ * adds them in slot order and writes the gradient, so the results stay
+ * deterministic (they differ from an uncut run only in the order of fp32
+ * additions).  Plus a small clear of the arrival counters when a schedule
+ * cuts anything.  No float atomics.
  */
 typedef struct {
   int32_t dtype;          /* BSATTN_BF16 */
@@ -341,10 +349,51 @@ typedef struct {
                              gradients are those of the function that forward computed (softmax
                              over its kept blocks; BLASST notes, training with the skipping
                              forward).  NULL = every visited block */
+  const int32_t* dq_items;  /* optional device copy of bsattn_build_schedule's items for the CSR
+                               (needs it); NULL = one dq work-group per tile, and the four dq_
+                               counts / merges below must be 0 / NULL */
+  int32_t dq_n_items;
+  const int32_t* dq_merges; /* device copy of that schedule's merges (NULL if dq_n_merges == 0) */
+  int32_t dq_n_merges;
+  int32_t dq_n_slots;
+  const int32_t* kv_items;  /* optional device copy of bsattn_build_dkdv_schedule's items for the
+                               CSC (needs it, with the same d); NULL = one dk/dv work-group per
+                               group of key blocks, and the kv_ counts / merges must be 0 / NULL */
+  int32_t kv_n_items;
+  const int32_t* kv_merges; /* device copy of its merges (NULL if kv_n_merges == 0) */
+  int32_t kv_n_merges;
+  int32_t kv_n_slots;
 } bsattn_prefill_bwd_args;
 
-/* Workspace bytes of a backward call (one float per query row and head). */
-size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Nq);
+/* Workspace bytes of a backward call: one float per query row and head,
+ * plus the partial sums and arrival counters of the schedules' slots
+ * (dq_n_slots, kv_n_slots: 0 without a schedule).  0 for an invalid shape.
+ * Calls may share a workspace (no initial contents are needed; the counters
+ * are cleared by the call) if they do not overlap. */
+size_t bsattn_prefill_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq, int32_t d,
+                                         int32_t dq_n_slots, int32_t kv_n_slots);
+
+/*
+ * Schedule of the backward dK/dV kernel over the CSC (col_ptr [Tc + 1],
+ * row_idx: ascending query tiles per key block, bsattn_transpose_block_index)
+ * for G query heads per K/V head and head dim d (which fixes the key blocks
+ * per work-group: 1 at d = 64, 2 at d = 128).  A group of blocks visits, for
+ * each query head, every tile of the union of its blocks' lists: G * |union|
+ * positions.  A group with more than max_positions_per_item positions is cut
+ * into near-equal chunks of consecutive positions.
+ *   items  [n_items][8]  {group, first position, end position, head of the
+ *                        first position, list positions (block 0, block 1)
+ *                        of its tile, slot, merge}; slot = merge = -1: the
+ *                        item writes dk/dv directly; longest first
+ *   merges [n_merges][3] {group, first slot, number of slots}
+ * Every group gets an item (one with no position writes zeros).  Two-call
+ * pattern as bsattn_build_schedule.  Host buffers.  INVALID_ARG if col_ptr
+ * decreases or a list is not strictly ascending.
+ */
+bsattn_status bsattn_build_dkdv_schedule(const int32_t* col_ptr, const int32_t* row_idx, int32_t Tc, int32_t G,
+                                         int32_t d, int32_t max_positions_per_item, int32_t* items,
+                                         int32_t items_capacity, int32_t* merges, int32_t merges_capacity,
+                                         int32_t* n_items, int32_t* n_merges, int32_t* n_slots);
 
 /* Enqueue the backward on `stream`.  Validation as for the forward (pointers
  * non-null and 16-byte aligned, strides multiples of 8 elements, d

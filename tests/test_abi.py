@@ -87,7 +87,7 @@ def _good_bwd():
         getattr(a, fld)[:] = [256 * h * 128, h * 128, 128]
     a.scale, a.Br, a.Bc = 0.088, 128, 64
     a.workspace = 0x100000
-    a.workspace_bytes = bsa.prefill_bwd_workspace_size(2, 8, 256)
+    a.workspace_bytes = bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 128)
     return a
 
 
@@ -106,7 +106,33 @@ BAD_BWD = [
     ("Br 64", lambda a: setattr(a, "Br", 64), _abi.BSATTN_ERR_UNSUPPORTED),
     ("workspace small", lambda a: setattr(a, "workspace_bytes", 64), _abi.BSATTN_ERR_CAPACITY),
     ("workspace misaligned", lambda a: setattr(a, "workspace", 0x100010), _abi.BSATTN_ERR_INVALID_ARG),
+    ("dq schedule without CSR", lambda a: (setattr(a, "dq_items", FAKE), setattr(a, "dq_n_items", 4)),
+     _abi.BSATTN_ERR_INVALID_ARG),
+    ("kv schedule without CSC", lambda a: (setattr(a, "kv_items", FAKE), setattr(a, "kv_n_items", 4)),
+     _abi.BSATTN_ERR_INVALID_ARG),
+    ("dq slots without items", lambda a: setattr(a, "dq_n_slots", 2), _abi.BSATTN_ERR_INVALID_ARG),
+    ("kv merges without merge array", lambda a: (_with_index(a), setattr(a, "kv_items", FAKE),
+                                                 setattr(a, "kv_n_items", 3), setattr(a, "kv_n_merges", 1),
+                                                 setattr(a, "kv_n_slots", 2)), _abi.BSATTN_ERR_INVALID_ARG),
+    ("dq slots beyond workspace", lambda a: (_with_index(a), setattr(a, "dq_items", FAKE), setattr(a, "dq_n_items", 3),
+                                             setattr(a, "dq_merges", FAKE), setattr(a, "dq_n_merges", 1),
+                                             setattr(a, "dq_n_slots", 2)), _abi.BSATTN_ERR_CAPACITY),
 ]
+
+
+def _with_index(a):
+    a.row_ptr = a.col_idx = a.col_ptr = a.row_idx = FAKE
+
+
+def test_backward_workspace_covers_schedule_slots():
+    base = bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 128)
+    assert base >= 2 * 8 * 256 * 4
+    # dQ partials: 128 rows x d floats per slot, batch and head; dK/dV: 2 blocks x 64 keys x d x 2 at d = 128
+    assert bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 128, dq_n_slots=3) >= base + 3 * 2 * 8 * 128 * 128 * 4
+    assert bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 128, kv_n_slots=5) >= base + 5 * 2 * 2 * 2 * 64 * 128 * 2 * 4
+    assert bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 64, kv_n_slots=5) >= 5 * 2 * 2 * 1 * 64 * 64 * 2 * 4
+    assert bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 96) == 0
+    assert bsa.prefill_bwd_workspace_size(2, 8, 2, 256, 128, dq_n_slots=-1) == 0
 
 
 @pytest.mark.parametrize("name,mutate,status", BAD_BWD, ids=[b[0] for b in BAD_BWD])

@@ -192,6 +192,60 @@ def test_prefill_group_major():
         bsa.prefill_group_major(1, 8, 3, 128, 10)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 3])
+def test_dkdv_schedule_covers_every_position_once(d, G):
+    c3 = get_config("cfg3")
+    rp, ci = bsa.build_block_index(c3.mask, c3.N, c3.N, 128, 64)
+    Tc = c3.N // 64
+    cp, ri = bsa.transpose_block_index(rp, ci, Tc)
+    NB = 1 if d == 64 else 2
+    for mx in (7, 100, 1 << 30):
+        sc = bsa.build_dkdv_schedule(cp, ri, G, d, mx)
+        assert sc.items.shape[1] == 8
+        lens = (sc.items[:, 2] - sc.items[:, 1]).tolist()
+        assert lens == sorted(lens, reverse=True)                      # longest first
+        by_group = {}
+        for it in sc.items.tolist():
+            by_group.setdefault(it[0], []).append(it)
+        assert sorted(by_group) == list(range(-(-Tc // NB)))           # every group has an item
+        slots = []
+        for m, its in by_group.items():
+            lists = [ri[cp[j]:cp[j + 1]].tolist() for j in range(NB * m, min(NB * m + NB, Tc))]
+            uni = sorted(set().union(*map(set, lists)))
+            P = G * len(uni)
+            its.sort(key=lambda x: x[1])
+            assert its[0][1] == 0 and its[-1][2] == P                  # the positions, partitioned
+            assert all(a[2] == b[1] for a, b in zip(its, its[1:]))
+            assert all(x[2] - x[1] <= mx for x in its)
+            if len(its) == 1 and its[0][6] < 0:
+                continue
+            for m_, p0, p1, hc, i0, i1, slot, mrg in its:                # chunks: the cursor at p0
+                t0 = uni[p0 % len(uni)]
+                assert hc == p0 // len(uni)
+                assert i0 == sum(1 for t in lists[0] if t < t0)
+                assert i1 == (sum(1 for t in lists[1] if t < t0) if len(lists) > 1 else 0)
+                mt, s0, n = sc.merges[mrg]
+                assert mt == m and s0 <= slot < s0 + n and n == len(its)
+                slots.append(slot)
+        assert sorted(slots) == list(range(sc.n_slots))
+    assert bsa.build_dkdv_schedule(cp, ri, G, d, 1 << 30).n_slots == 0
+
+
+def test_dkdv_schedule_validation():
+    cp = np.array([0, 2, 3], np.int32)
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_dkdv_schedule(cp, np.array([1, 0, 0], np.int32), 1, 128, 4)   # list not ascending
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_dkdv_schedule(np.array([0, 2, 1], np.int32), np.array([0, 1], np.int32), 1, 128, 4)
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_dkdv_schedule(cp, np.array([0, 1, 0], np.int32), 1, 96, 4)    # head dim
+    with pytest.raises(bsa.BsattnError):
+        bsa.build_dkdv_schedule(cp, np.array([0, 1, 0], np.int32), 1, 64, 0)    # max positions < 1
+    sc = bsa.build_dkdv_schedule(np.array([0, 0, 0], np.int32), np.zeros(0, np.int32), 2, 64, 4)
+    assert sc.items.tolist() == [[0, 0, 0, 0, 0, 0, -1, -1], [1, 0, 0, 0, 0, 0, -1, -1]]  # empty blocks: zeros
+
+
 def test_schedule_validation():
     import ctypes as C
     from block_sparse_attention_flash_amd import _abi

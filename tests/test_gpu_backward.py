@@ -41,7 +41,19 @@ def _cfg(N=300, d=128, Hq=4, Hkv=2, seed=201, generator="iid", causal=False, mas
                            causal=causal, lam=0.0, mask=mask, seed=seed, generator=generator)
 
 
-def run_fwd_bwd(cfg, q, k, v, dout, csr=None, n_valid=None):
+def bwd_schedule(csr, B, Hq, Hkv, d, N, schedule):
+    """None; "default" (default_bwd_schedule); or (dq max blocks, dK/dV max
+    positions) per item, small bounds forcing many chunks."""
+    if schedule is None:
+        return None
+    colp, rowi = bsa.transpose_block_index(csr[0], csr[1], -(-N // 64))
+    if schedule == "default":
+        return bsa.default_bwd_schedule(csr[0], colp, rowi, B, Hq, Hkv, d)
+    dq_max, kv_max = schedule
+    return bsa.BwdSchedule(bsa.build_schedule(csr[0], dq_max), bsa.build_dkdv_schedule(colp, rowi, Hq // Hkv, d, kv_max))
+
+
+def run_fwd_bwd(cfg, q, k, v, dout, csr=None, n_valid=None, schedule=None):
     """Forward (with lse) then backward on the GPU; host copies of everything."""
     B, N, Hq, d = q.shape
     Tc = -(-N // 64)
@@ -50,11 +62,15 @@ def run_fwd_bwd(cfg, q, k, v, dout, csr=None, n_valid=None):
         colp, rowi = bsa.transpose_block_index(csr[0], csr[1], Tc)
         rp, ci = torch.from_numpy(csr[0]).to(DEV), torch.from_numpy(csr[1]).to(DEV)
         cp, ri = torch.from_numpy(colp).to(DEV), torch.from_numpy(rowi).to(DEV)
+    sched = bwd_schedule(csr, B, Hq, k.shape[2], d, N, schedule)
+    if sched is not None:
+        _say(f"  schedule: dq {sched.dq.n_items} items / {sched.dq.n_slots} slots, "
+             f"dk/dv {sched.kv.n_items} items / {sched.kv.n_slots} slots")
     nv = cfg.n_valid if n_valid is None else n_valid
     lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=DEV)
     out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, row_ptr=rp, col_idx=ci, n_valid=nv, lse=lse)
     dq, dk, dv = bsa.prefill_bwd(q, k, v, out, dout, lse, scale=cfg.scale, causal=cfg.causal, row_ptr=rp,
-                                 col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=nv)
+                                 col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=nv, schedule=sched)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu().numpy(), dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -80,9 +96,9 @@ def compare_grad(got, ref, what):
     assert err.mean() <= MEAN_REL * s, f"{what}: mean-abs {err.mean():.3e} > {MEAN_REL * s:.3e}"
 
 
-def check_all(cfg, q, k, v, dout, csr=None, n_valid=None):
+def check_all(cfg, q, k, v, dout, csr=None, n_valid=None, schedule=None):
     nv = cfg.n_valid if n_valid is None else n_valid
-    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr, nv)
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr, nv, schedule)
     mask = token_mask(cfg.N, csr, nv, cfg.causal)
     rq, rk, rv = BW.prefill_grads(q, k, v, dout, mask, cfg.scale)
     rl = BW.prefill_lse(q, k, mask, cfg.scale)
@@ -144,6 +160,31 @@ def test_backward_dit_mask(d):
     check_all(cfg, q, k, v, dout, csr)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ["csr", "csr_causal_nvalid", "dit"])
+def test_backward_schedule_forced_chunks(case, d):
+    """Schedules with tiny bounds (dQ: 2 blocks per item; dK/dV: 3 (head,
+    tile) positions per item), so nearly every tile and key block is cut
+    into chunks whose partials the last arriving chunk adds up, and dK/dV
+    chunks start mid-way through a head's list (GQA, two query heads per K/V
+    head)."""
+    causal = "causal" in case
+    if case == "dit":
+        spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+        n = spec.n_valid + 13
+        cfg = _cfg(N=n, d=d, Hq=4, Hkv=2, generator="iid", seed=271, mask=spec)
+        csr = bsa.build_block_index(spec, n, n, 128, 64)
+        n_valid = None
+    else:
+        cfg = _cfg(d=d, causal=causal, seed=281 + d)
+        csr = _random_csr(3, 5, 17 + d)
+        n_valid = 280 if "nvalid" in case else 300
+    _say(f"backward with forced chunks: {case} d{d}")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    check_all(cfg, q, k, v, dout, csr, n_valid, schedule=(2, 3))
+
+
 def test_backward_deterministic():
     cfg = _cfg(N=700, d=128, Hq=8, Hkv=2, seed=221, causal=True)
     _say("backward determinism")
@@ -171,16 +212,19 @@ def test_backward_deterministic_under_full_load(d):
             assert torch.equal(x, y)
 
 
-def test_backward_cfg2_full_size_sampled():
+@pytest.mark.parametrize("schedule", [None, "default"])
+def test_backward_cfg2_full_size_sampled(schedule):
     """The DiT image+text workload at full size (B 2, H 16, N 4352, d 64):
     every gradient of two (batch, head) pairs against the oracle run on that
-    head alone (dK and dV of a head depend only on that head when Hq = Hkv)."""
+    head alone (dK and dV of a head depend only on that head when Hq = Hkv),
+    without and with the default schedule (which cuts the anchor rows and
+    the anchor key block)."""
     cfg = get_config("cfg2")
-    _say("backward cfg2 full size, heads (0, 3) and (1, 12)")
+    _say(f"backward cfg2 full size, heads (0, 3) and (1, 12), schedule {schedule}")
     q, k, v = gen_prefill_inputs(cfg)
     dout = gen_prefill_grad_output(cfg)
     csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
-    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr)
+    out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr, schedule=schedule)
     mask = token_mask(cfg.N, csr, cfg.n_valid, False)
     for b, h in ((0, 3), (1, 12)):
         sl = lambda x: x[b:b + 1, :, h:h + 1]
@@ -286,3 +330,41 @@ def test_empty_block_index():
     out, lse, dq, dk, dv = run_fwd_bwd(cfg, q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), csr)
     assert torch.all(out == 0) and np.all(np.isneginf(lse))
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_backward_cfg3_schedule_full_size():
+    """The video DiT workload at full size (B 1, H 24, N 65920, d 128) with
+    the default schedule: the text query tiles (every key block) and the
+    anchor key block (every query tile) are cut into many chunks.  The dQ
+    rows of the three text tiles of head 0 against the oracle on those rows
+    (a dQ row depends only on its own row); all gradients against the
+    unscheduled run, which may differ only in the order of fp32 additions;
+    and two scheduled runs bit-identical."""
+    cfg = get_config("cfg3")
+    _say("backward cfg3 full size, default schedule against none")
+    q, k, v = gen_prefill_inputs(cfg)
+    dout = gen_prefill_grad_output(cfg)
+    csr = bsa.build_block_index(cfg.mask, cfg.N, cfg.N, 128, 64)
+    qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, dout))
+    plain = run_fwd_bwd(cfg, qd, kd, vd, gd, csr)
+    sched = run_fwd_bwd(cfg, qd, kd, vd, gd, csr, schedule="default")
+    again = run_fwd_bwd(cfg, qd, kd, vd, gd, csr, schedule="default")
+    for x, y in zip(sched[2:], again[2:]):
+        assert torch.equal(x, y)
+    for name, x, y in zip(("dq", "dk", "dv"), sched[2:], plain[2:]):
+        xf, yf = x.float(), y.float()
+        s = float(yf.abs().max())
+        err = (xf - yf).abs()
+        _say(f"  {name}: scheduled against unscheduled max-abs {float(err.max()):.3e} ({float(err.max()) / s:.2e} s)")
+        assert float(err.max()) <= 2.0 ** -6 * s and float(err.mean()) <= 2.0 ** -11 * s
+    Tr = cfg.N // 128
+    tm = np.zeros((Tr, cfg.N // 64), bool)
+    for t in range(Tr):
+        tm[t, csr[1][csr[0][t]:csr[0][t + 1]]] = True
+    dq = sched[2]
+    for t in (Tr - 3, Tr - 2, Tr - 1):
+        rows = slice(128 * t, 128 * t + 128)
+        allowed = M.expand_token_mask(tm[t:t + 1], 128, cfg.N, 128, 64, cfg.n_valid, False)
+        hq, _, _ = BW.masked_attention_grads(q[0, rows, 0], k[0, :, 0], v[0, :, 0], dout[0, rows, 0], allowed,
+                                             cfg.scale)
+        compare_grad(dq[0, rows, 0], hq, f"dq tile {t} head 0")
