@@ -24,6 +24,13 @@
 // dS never leave registers.  Each kernel owns its outputs: no atomics, and
 // the results do not depend on scheduling.
 //
+// Optional schedules cut the longest walks (a tile whose list holds every
+// key block, a key block every tile attends) into chunks of the list, or of
+// the (query head, tile) positions of a key-block group: a chunk writes its
+// fp32 accumulators to a workspace slot and the last chunk to arrive adds
+// the slots in slot order (DiT article section 5.3: uneven rows unbalance
+// the GPU).  The sums stay deterministic.
+//
 // The pages print no backward pass; the gradients are the chain rule on the
 // forward's definition (the DiT article trains with the block-sparse
 // forward, section 4; its section 3.3 check of the block list before any

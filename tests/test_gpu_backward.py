@@ -185,6 +185,45 @@ def test_backward_schedule_forced_chunks(case, d):
     check_all(cfg, q, k, v, dout, csr, n_valid, schedule=(2, 3))
 
 
+def test_backward_plan_and_graph_replays():
+    """The backward with schedules that cut (forced tiny chunks) captured in a
+    HIP graph: its arrival counters are cleared by a fill kernel each call,
+    so every replay, with other GPU work between replays, equals the eager
+    result bit for bit."""
+    spec = dit_image_text_spec(grid=16, text=40, radius=2, anchors=8, unit=16)
+    n = spec.n_valid + 13
+    cfg = _cfg(N=n, d=128, Hq=4, Hkv=2, generator="iid", seed=291, mask=spec)
+    _say("backward plan + graph, schedules with cut tiles and key blocks")
+    q, k, v = (x.to(DEV) for x in gen_prefill_inputs(cfg))
+    dout = gen_prefill_grad_output(cfg).to(DEV)
+    csr = bsa.build_block_index(spec, n, n, 128, 64)
+    colp, rowi = bsa.transpose_block_index(csr[0], csr[1], -(-n // 64))
+    sched = bwd_schedule(csr, 2, 4, 2, 128, n, (2, 3))
+    assert sched.dq.n_merges > 0 and sched.kv.n_merges > 0
+    rp, ci, cp, ri = (torch.from_numpy(x).to(DEV) for x in (csr[0], csr[1], colp, rowi))
+    lse = torch.empty((2, 4, n), dtype=torch.float32, device=DEV)
+    out = bsa.prefill_fwd(q, k, v, scale=cfg.scale, row_ptr=rp, col_idx=ci, n_valid=spec.n_valid, lse=lse)
+    kw = dict(scale=cfg.scale, row_ptr=rp, col_idx=ci, col_ptr=cp, row_idx=ri, n_valid=spec.n_valid, schedule=sched)
+    ref = [x.clone() for x in bsa.prefill_bwd(q, k, v, out, dout, lse, **kw)]
+    plan = bsa.prefill_bwd_plan(q, k, v, out, dout, lse, **kw)
+    got = plan()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    for r in range(3):
+        for x in plan.out:
+            x.fill_(3.0)
+        junk = torch.randn(1 << 20, device=DEV).sum()   # unrelated work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(plan.out, ref):
+            assert torch.equal(x, y), r
+    del junk
+
+
 def test_backward_deterministic():
     cfg = _cfg(N=700, d=128, Hq=8, Hkv=2, seed=221, causal=True)
     _say("backward determinism")
