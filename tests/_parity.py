@@ -20,7 +20,7 @@ BF16_MAX, BF16_MEAN, FP32_MAX = 1e-2, 1e-3, 1e-5
 MARGIN = 1e-3
 
 
-def compare_out(got, ref, fp32: bool, what: str):
+def compare_out(got, ref, fp32: bool, what: str, bf16_mean: float = BF16_MEAN):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -28,13 +28,13 @@ def compare_out(got, ref, fp32: bool, what: str):
         assert err.max() <= FP32_MAX, f"{what}: fp32 max-abs {err.max():.3e}"
     else:
         assert err.max() <= BF16_MAX, f"{what}: bf16 max-abs {err.max():.3e}"
-        assert err.mean() <= BF16_MEAN, f"{what}: bf16 mean-abs {err.mean():.3e}"
+        assert err.mean() <= bf16_mean, f"{what}: bf16 mean-abs {err.mean():.3e}"
     return float(err.max()), float(err.mean())
 
 
 def check_prefill_tile(q, k, v, out_gpu, state_gpu, counters_gpu, b, h, t, *, Br, Bc, scale, causal, lam,
                        n_valid, row_ptr=None, col_idx=None, fp32=False, rows_limit=None, method="loop",
-                       order="ascending"):
+                       order="ascending", bf16_mean=BF16_MEAN):
     """Oracle for one (b, h, t); compares visited set, skip set, counters and the output rows.
 
     q/k/v/out_gpu/state_gpu/counters_gpu are host tensors or arrays.  Returns
@@ -60,5 +60,5 @@ def check_prefill_tile(q, k, v, out_gpu, state_gpu, counters_gpu, b, h, t, *, Br
     assert c[0] == len(blocks) and c[1] == int(g_skip.sum()), f"counters {c} at b{b} h{h} t{t}"
     got = A.as_f64(out_gpu[b, rows[0]:rows[-1] + 1, h])
     keep = slice(None) if rows_limit is None else (rows < rows_limit)
-    compare_out(got[keep], ref[keep], fp32, f"b{b} h{h} t{t}")
+    compare_out(got[keep], ref[keep], fp32, f"b{b} h{h} t{t}", bf16_mean)
     return len(blocks), int(g_skip.sum()), int(excused.sum())
