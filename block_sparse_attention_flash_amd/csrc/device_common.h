@@ -35,14 +35,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// ds_read_b64_tr_b16 on an LDS address.  Within each group of 16 lanes, lane
-// j receives, in slot s (0..3), the 16-bit element j%4 of the 8 bytes
-// addressed by lane 4*s + j/4 of the same group.  (Checked on the device.)
-__device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* lds_ptr) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
-}
-
+// ds_read_b64_tr_b16 (issued from inline asm by the kernels): within each
+// group of 16 lanes, lane j receives, in slot s (0..3), the 16-bit element
+// j%4 of the 8 bytes addressed by lane 4*s + j/4 of the same group.
+// (Checked on the device.)  Two such reads, of keys r and r + 8, joined
+// below, give one 8-element MFMA operand.
 __device__ __forceinline__ bf16x8 join_bf16x4(i16x4 lo, i16x4 hi) {
   union {
     i16x4 h[2];

@@ -87,8 +87,6 @@ struct Smem {
   int vote[2][4];  // [0][w]: wave w's vote word on the current block; also scratch after the loop
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data
 // format, no swizzle; range checking against num_records).
 constexpr int kBufferWord3 = 0x00020000;
