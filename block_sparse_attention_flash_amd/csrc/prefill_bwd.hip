@@ -5,7 +5,8 @@
 // token-level valid-length and causal limits), with P rebuilt from the
 // forward's per-row log-sum-exp:
 //
-//   dot   Dv[i] = sum_c dout[i][c] out[i][c]            (one float per row)
+//   dot   Dv[i] = sum_c dout[i][c] out[i][c]            (one float per row;
+//         the same launch zeroes the schedules' arrival counters)
 //   dkdv  per (batch, K/V head, key block j): walk the query tiles whose CSR
 //         list holds j (the transposed index), for every query head of the
 //         group, and accumulate in registers
@@ -102,6 +103,18 @@ __global__ __launch_bounds__(NT) void bwd_dot_kernel(const BwdParams p) {
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o);
   if (rid < total && c == 0) p.dvec[rid] = acc;
+  // the schedules' arrival counters sit at offsets that depend on the call's
+  // shape, so a shared workspace may hold any bytes there: zero them here,
+  // ahead of the kernels that count with them
+  const int64_t nthreads = (int64_t)gridDim.x * NT;
+  if (p.dq_arrive) {
+    const int64_t n = (int64_t)p.dq_n_merges * p.B * p.Hq;
+    for (int64_t i = gid; i < n; i += nthreads) p.dq_arrive[i] = 0;
+  }
+  if (p.kv_arrive) {
+    const int64_t n = (int64_t)p.kv_n_merges * p.B * p.Hkv;
+    for (int64_t i = gid; i < n; i += nthreads) p.kv_arrive[i] = 0;
+  }
 }
 
 // Store 4 consecutive d values (accumulator elements 4q..4q+3 of tile n) as bf16.
@@ -445,34 +458,60 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
       const int r0 = 32 * qh;
       const __bf16* sq = sm.q[buf];
       const __bf16* sg = sm.g[buf];
+      const __bf16* skb = sm.k[kb];
+      const __bf16* svb = sm.v[kb];
       f32x16 s = f32x16{}, dp = f32x16{};
       bf16x8 frg[NTD], frq[NTD], dbp = bf16x8{};
 #pragma unroll
       for (int n = 0; n < NTD; ++n) frq[n] = bf16x8{};
+      // S = Q K^T and dP = dO V^T: each pair of fragments is read for the
+      // next key step as soon as the product that used it has issued, so the
+      // read runs under the other chain's product
+      bf16x8 fq = read_row<D>(sq, r0 + l32, 0, hi), fk = read_row<D>(skb, 32 * kh + l32, 0, hi);
+      bf16x8 fg = read_row<D>(sg, r0 + l32, 0, hi), fv = read_row<D>(svb, 32 * kh + l32, 0, hi);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row<D>(sq, r0 + l32, ks, hi), read_row<D>(sm.k[kb], 32 * kh + l32, ks, hi), s);
-        dp = mfma32(read_row<D>(sg, r0 + l32, ks, hi), read_row<D>(sm.v[kb], 32 * kh + l32, ks, hi), dp);
-        if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        s = mfma32(fq, fk, s);
+        if (ks + 1 < KS) {
+          fq = read_row<D>(sq, r0 + l32, ks + 1, hi);
+          fk = read_row<D>(skb, 32 * kh + l32, ks + 1, hi);
+        }
+        dp = mfma32(fg, fv, dp);
+        if (ks + 1 < KS) {
+          fg = read_row<D>(sg, r0 + l32, ks + 1, hi);
+          fv = read_row<D>(svb, 32 * kh + l32, ks + 1, hi);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        // P and dS of this lane's 8 (row, key) pairs of the key step: rows
+        // r0 + 16 kk + 8 q + 4 hi + (0..3), q = 0, 1, whose lse and Dv come in
+        // four-row vector reads; masked pairs take 0 by a select (no branch)
         float pv[8], dsv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int a = 8 * kk + i;
-          const int rl = r0 + 8 * (a >> 2) + 4 * hi + (a & 3);
-          const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
-          pv[i] = ok ? fast_exp2(fmaf(s[a], c2, -sm.lse[buf][rl] * kLog2e)) : 0.0f;
-          dsv[i] = pv[i] * (dp[a] - sm.dvec[buf][rl]);
+        for (int q = 0; q < 2; ++q) {
+          const int rb = r0 + 16 * kk + 8 * q + 4 * hi;
+          const float4 l4 = *reinterpret_cast<const float4*>(sm.lse[buf] + rb);
+          const float4 d4 = *reinterpret_cast<const float4*>(sm.dvec[buf] + rb);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * q + u, a = 8 * kk + i, rl = rb + u;
+            const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
+            const float e = fast_exp2(fmaf(s[a], c2, -lv[u] * kLog2e));
+            pv[i] = ok ? e : 0.0f;
+            dsv[i] = pv[i] * (dp[a] - dvv[u]);
+          }
         }
         const bf16x8 pb = to_bf16x8(pv);
         const bf16x8 db = to_bf16x8(dsv);
-        // (the first read follows the dK products of the previous step; the
-        // S and dP products before the first step have been waited for)
+        // (key step 1: the operands of key step 0's dK products; key step 0:
+        // nothing, the S and dP products having been waited for)
         read_tr_xn<D>(frg, sg, r0 + 16 * kk, lane, frq, dbp);
 #pragma unroll
         for (int n = 0; n < NTD; ++n) dv[n] = mfma32(frg[n], pb, dv[n]);  // dV^T += dO^T P
+        __builtin_amdgcn_sched_barrier(0);  // the dV products issue before the Q^T reads
         read_tr_xn<D>(frq, sq, r0 + 16 * kk, lane, frg, pb);
 #pragma unroll
         for (int n = 0; n < NTD; ++n) dk[n] = mfma32(frq[n], db, dk[n]);  // dK^T += Q^T dS
@@ -585,14 +624,24 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
 template <int D>
 constexpr int kDqBlocksPerCu = D == 64 ? 3 : 2;
 
+// the dQ kernel's LDS: two stages of one key block's K and V, and a chunk's
+// arrival ticket.  One structure: with K and V as two separate arrays the
+// compiler waited for the next block's global->LDS loads before the first
+// read of the current block (it could not tell the two stages of an array
+// apart), which took the prefetch off the loop.
+template <int D>
+struct DqSmem {
+  __bf16 k[2][BC * D];
+  __bf16 v[2][BC * D];
+  int ticket;
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 16;
   constexpr int NTD = D / 32;
-  __shared__ __bf16 smk[2][BC * D];
-  __shared__ __bf16 smv[2][BC * D];
-  __shared__ int ticket;
+  __shared__ DqSmem<D> sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -664,8 +713,8 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.ks_b + (int64_t)g * p.ks_h;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.vs_b + (int64_t)g * p.vs_h;
   auto fetch = [&](int buf, int j) __attribute__((always_inline)) {
-    dma_tile64<D>(smk[buf], kbase, p.Nk, p.ks_t, j * BC, wave, lane);
-    dma_tile64<D>(smv[buf], vbase, p.Nk, p.vs_t, j * BC, wave, lane);
+    dma_tile64<D>(sm.k[buf], kbase, p.Nk, p.ks_t, j * BC, wave, lane);
+    dma_tile64<D>(sm.v[buf], vbase, p.Nk, p.vs_t, j * BC, wave, lane);
   };
   f32x16 dq[NTD];
 #pragma unroll
@@ -674,9 +723,6 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
   const uint8_t* skipped = p.block_state ? p.block_state + (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc : nullptr;
   int j = blk(e0), jn = blk(e0 + 1);
   if (e0 < e1) fetch(0, j);
-  bf16x8 fa[NTD], fb[NTD], dbp = bf16x8{};
-#pragma unroll
-  for (int n = 0; n < NTD; ++n) fb[n] = bf16x8{};
   for (int e = e0; e < e1; ++e) {
     const int buf = (e - e0) & 1;
     // block e has landed in every wave, and every wave is done with block e - 1
@@ -686,15 +732,26 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
     j = jn;
     jn = blk(e + 2);
     if (skipped && skipped[jc] == 2) continue;  // the forward skipped it: no gradient (uniform branch)
-    const __bf16* sk = smk[buf];
-    const __bf16* sv = smv[buf];
+    const __bf16* sk = sm.k[buf];
+    const __bf16* sv = sm.v[buf];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the block
       f32x16 s = f32x16{}, dp = f32x16{};
+      // S^T[key][q] and dP^T[key][q], alternating; each K or V fragment is
+      // read RA products ahead, into the register its product RA back used
+      constexpr int NP = 2 * KS, RA = 2;
+      auto frag = [&](int i) __attribute__((always_inline)) {
+        return read_row<D>((i & 1) ? sv : sk, 32 * mt + l32, i >> 1, hi);
+      };
+      bf16x8 ring[RA];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row<D>(sk, 32 * mt + l32, ks, hi), qf[ks], s);   // S^T[key][q]
-        dp = mfma32(read_row<D>(sv, 32 * mt + l32, ks, hi), gf[ks], dp);  // dP^T[key][q]
+      for (int i = 0; i < RA; ++i) ring[i] = frag(i);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        if (i & 1) dp = mfma32(ring[i % RA], gf[i >> 1], dp);
+        else s = mfma32(ring[i % RA], qf[i >> 1], s);
+        if (i + RA < NP) ring[i % RA] = frag(i + RA);
+        __builtin_amdgcn_sched_barrier(0);
       }
       float dsv[16];
 #pragma unroll
@@ -705,13 +762,21 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
         dsv[a] = pr * (dp[a] - dvr);
       }
       const bf16x8 d0 = to_bf16x8(dsv), d1 = to_bf16x8(dsv + 8);
-      read_tr_xn<D>(fa, sk, 32 * mt, lane, fb, dbp);
+      // No product is in flight at this read: d0 comes from the results of
+      // the last S and dP products, and a wave's products finish in the
+      // order they were issued.  d0 fills the busy list so that the read
+      // stays after that computation.
+      bf16x8 dep[NTD];
+#pragma unroll
+      for (int n = 0; n < NTD; ++n) dep[n] = d0;
+      bf16x8 fa[NTD], fb[NTD];
+      read_tr_xn<D>(fa, sk, 32 * mt, lane, dep, d0);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fa[n], d0, dq[n]);
+      __builtin_amdgcn_sched_barrier(0);
       read_tr_xn<D>(fb, sk, 32 * mt + 16, lane, fa, d0);
 #pragma unroll
       for (int n = 0; n < NTD; ++n) dq[n] = mfma32(fb[n], d1, dq[n]);
-      dbp = d1;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -735,9 +800,9 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
     }
     wait_stores_done();
     __syncthreads();  // every wave's partial has completed
-    if (tid == 0) ticket = atomicAdd(p.dq_arrive + ((int64_t)mrg * p.B + b) * p.Hq + h, 1);
+    if (tid == 0) sm.ticket = atomicAdd(p.dq_arrive + ((int64_t)mrg * p.B + b) * p.Hq + h, 1);
     __syncthreads();
-    if (ticket != ns - 1) return;  // a later chunk adds them up
+    if (sm.ticket != ns - 1) return;  // a later chunk adds them up
 #pragma unroll
     for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
     for (int sl = s0; sl < s0 + ns; ++sl) {
@@ -760,10 +825,6 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
 }
 
 // Zero n words (the chunk arrival counters of the schedules).
-__global__ __launch_bounds__(NT) void bwd_clear_kernel(int32_t* w, int n) {
-  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) w[i] = 0;
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
@@ -771,15 +832,6 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)dot_blocks), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the arrival counters sit at offsets that depend on the call's shape, so
-  // a shared workspace may hold any bytes there: zero them first
-  const struct { int32_t* w; int n; } clears[] = {{p.dq_arrive, p.dq_n_merges * p.B * p.Hq},
-                                                  {p.kv_arrive, p.kv_n_merges * p.B * p.Hkv}};
-  for (const auto& c : clears) {
-    if (!c.w || c.n == 0) continue;
-    hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)min(64, (c.n + NT - 1) / NT)), dim3(NT), 0, s, c.w, c.n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   constexpr int NB = kDkdvBlocks<D>;
   const int64_t kv_units = p.kv_items ? p.kv_n_items : (p.Tc + NB - 1) / NB;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.B * p.Hkv * kv_units)), dim3(256 * NB),
