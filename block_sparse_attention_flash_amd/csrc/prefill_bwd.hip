@@ -80,6 +80,18 @@ __device__ __forceinline__ uint32_t lds_addr_b(const void* ptr) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(ptr);
 }
 
+// Byte i of a block-state array, at a wave-uniform index, through the scalar
+// cache: the aligned word that holds it is read (a word never straddles a
+// page, so this stays inside the array's page) and the byte taken out.  A
+// vector byte load would be waited for with vmcnt, which also waits for
+// the next stage's loads in flight.
+__device__ __forceinline__ int state_byte(const uint8_t* base, int64_t i) {
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(base) + (uintptr_t)i;
+  const uint32_t w = *reinterpret_cast<const_u32_ptr>(a & ~(uintptr_t)3);
+  return (int)((w >> (8 * (a & 3))) & 0xffu);
+}
+
 // Dv = rowsum(dout * out), fp32, one row per D/8 lanes.
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_dot_kernel(const BwdParams p) {
@@ -369,7 +381,7 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
     const int row0 = t * BR + 64 * hf;
     if (jb >= p.Tc || row0 >= p.Nq) return false;
     if (CAUSAL && row0 + 63 < jb * BC) return false;
-    if (p.block_state && p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + jb] == 2) return false;
+    if (p.block_state && state_byte(p.block_state, (((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + jb) == 2) return false;
     return true;
   };
   // tile at the cursor and which blocks' lists hold it (-1: head exhausted)
@@ -731,7 +743,7 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
     const int jc = j;
     j = jn;
     jn = blk(e + 2);
-    if (skipped && skipped[jc] == 2) continue;  // the forward skipped it: no gradient (uniform branch)
+    if (skipped && state_byte(skipped, jc) == 2) continue;  // the forward skipped it: no gradient
     const __bf16* sk = sm.k[buf];
     const __bf16* sv = sm.v[buf];
 #pragma unroll
