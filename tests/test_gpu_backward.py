@@ -306,58 +306,76 @@ def test_backward_causal_gqa_loaded(d):
     compare_grad(dv[0, :, g], rv, f"dv g{g}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_backward_after_skipping_forward(d):
-    """BLASST forward (lambda > 0, causal GQA, the sink recipe so that blocks
-    are skipped), then the backward with that forward's block_state: the
-    gradients are those of softmax attention over each tile's kept blocks.
-    The oracle takes its own skip decisions (Algorithm 1); where a decision
-    lies within the accepted margin of the threshold it follows the GPU's,
-    as the forward tests do."""
+def _check_after_skipping_forward(N, Hq, Hkv, d, lam, seed, groups):
+    """BLASST forward (causal GQA, the sink recipe so that blocks are
+    skipped), then the backward with that forward's block_state: the
+    gradients of the K/V heads in ``groups`` and of their query heads are
+    those of softmax attention over each tile's kept blocks.  The oracle
+    takes its own skip decisions (Algorithm 1); where a decision lies within
+    the accepted margin of the threshold it follows the GPU's, as the
+    forward tests do.  Returns the number of blocks the forward skipped in
+    the checked heads."""
     from oracle import attention as A
     from _parity import MARGIN
-    N, lam = 1000, 0.3
-    cfg = PrefillWorkload(name="bwd_skip", description="", dtype="bf16", B=1, Hq=8, Hkv=2, N=N, d=d, Br=128,
-                          Bc=64, causal=True, lam=lam, mask=None, seed=231, generator="sink")
-    _say(f"backward after a skipping forward: causal GQA 8/2 N{N} d{d} lambda {lam}")
+    G = Hq // Hkv
+    cfg = PrefillWorkload(name="bwd_skip", description="", dtype="bf16", B=1, Hq=Hq, Hkv=Hkv, N=N, d=d, Br=128,
+                          Bc=64, causal=True, lam=lam, mask=None, seed=seed, generator="sink")
     q, k, v = gen_prefill_inputs(cfg)
     dout = gen_prefill_grad_output(cfg)
     qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, dout))
     Tr, Tc = -(-N // 128), -(-N // 64)
-    state = torch.zeros((1, 8, Tr, Tc), dtype=torch.uint8, device=DEV)
-    lse = torch.empty((1, 8, N), dtype=torch.float32, device=DEV)
+    state = torch.zeros((1, Hq, Tr, Tc), dtype=torch.uint8, device=DEV)
+    lse = torch.empty((1, Hq, N), dtype=torch.float32, device=DEV)
     out = bsa.prefill_fwd(qd, kd, vd, scale=cfg.scale, lam=lam, causal=True, block_state=state, lse=lse)
     dq, dk, dv = bsa.prefill_bwd(qd, kd, vd, out, gd, lse, scale=cfg.scale, causal=True, block_state=state)
     torch.cuda.synchronize()
     st = state.cpu().numpy()
     dq, dk, dv, lse = dq.cpu(), dk.cpu(), dv.cpu(), lse.cpu().numpy()
-    rq = np.zeros((1, N, 8, d))
-    rk = np.zeros((1, N, 2, d))
-    rv = np.zeros((1, N, 2, d))
     n_skip = 0
-    for h in range(8):
-        tm = np.zeros((Tr, Tc), bool)
-        for t in range(Tr):
-            rows, _, blocks, skip, margin = A.prefill_tile(q, k, v, 0, h, t, Br=128, Bc=64, scale=cfg.scale,
-                                                          causal=True, lam=lam, n_valid=N)
-            g_skip = st[0, h, t, blocks] == 2
-            bad = (g_skip != skip) & ~(np.abs(margin) <= MARGIN)
-            assert not bad.any(), f"skip set differs at h{h} t{t}"
-            tm[t, blocks[~g_skip]] = True          # oracle decisions, GPU's only inside the margin
-            n_skip += int(g_skip.sum())
-        mask = M.expand_token_mask(tm, N, N, 128, 64, N, True)
-        g = h // 4
-        hq, hk, hv = BW.masked_attention_grads(q[0, :, h], k[0, :, g], v[0, :, g], dout[0, :, h], mask, cfg.scale)
-        rq[0, :, h] = hq
-        rk[0, :, g] += hk
-        rv[0, :, g] += hv
-        rl = BW.row_lse(q[0, :, h], k[0, :, g], mask, cfg.scale)
-        assert np.abs(lse[0, h] - rl).max() <= LSE_ABS
+    for g in groups:
+        rk = np.zeros((N, d))
+        rv = np.zeros((N, d))
+        for h in range(G * g, G * g + G):
+            tm = np.zeros((Tr, Tc), bool)
+            for t in range(Tr):
+                rows, _, blocks, skip, margin = A.prefill_tile(q, k, v, 0, h, t, Br=128, Bc=64, scale=cfg.scale,
+                                                              causal=True, lam=lam, n_valid=N)
+                g_skip = st[0, h, t, blocks] == 2
+                bad = (g_skip != skip) & ~(np.abs(margin) <= MARGIN)
+                assert not bad.any(), f"skip set differs at h{h} t{t}"
+                tm[t, blocks[~g_skip]] = True          # oracle decisions, GPU's only inside the margin
+                n_skip += int(g_skip.sum())
+            mask = M.expand_token_mask(tm, N, N, 128, 64, N, True)
+            hq, hk, hv = BW.masked_attention_grads(q[0, :, h], k[0, :, g], v[0, :, g], dout[0, :, h], mask, cfg.scale)
+            compare_grad(dq[0, :, h], hq, f"dq h{h}")
+            rk += hk
+            rv += hv
+            rl = BW.row_lse(q[0, :, h], k[0, :, g], mask, cfg.scale)
+            assert np.abs(lse[0, h] - rl).max() <= LSE_ABS
+        compare_grad(dk[0, :, g], rk, f"dk g{g}")
+        compare_grad(dv[0, :, g], rv, f"dv g{g}")
+    return n_skip
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_after_skipping_forward(d):
+    """Causal GQA 8/2 at N 1000, lambda 0.3, every head checked."""
+    _say(f"backward after a skipping forward: causal GQA 8/2 N1000 d{d} lambda 0.3")
+    n_skip = _check_after_skipping_forward(1000, 8, 2, d, 0.3, 231, groups=(0, 1))
     _say(f"  blocks skipped by the forward: {n_skip}")
     assert n_skip > 0
-    compare_grad(dq, rq, "dq")
-    compare_grad(dk, rk, "dk")
-    compare_grad(dv, rv, "dv")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_after_skipping_forward_loaded(d):
+    """Causal GQA 32/8 at N 3072, lambda 0.5: launches that fill the GPU (the
+    dQ kernel runs 768 work-groups), so the skip-state reads of both
+    backward kernels run under the contention of a real launch.  Every
+    gradient of K/V head 3 and of its four query heads."""
+    _say(f"backward after a skipping forward: causal GQA 32/8 N3072 d{d} lambda 0.5, K/V head 3")
+    n_skip = _check_after_skipping_forward(3072, 32, 8, d, 0.5, 241 + d, groups=(3,))
+    _say(f"  blocks skipped by the forward in K/V head 3's query heads: {n_skip}")
+    assert n_skip > 0
 
 
 def test_empty_block_index():
