@@ -598,12 +598,21 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
       for (int sl = s0; sl < s0 + ns; ++sl) {
         const float* pp = part(sl);
 #pragma unroll
-        for (int n = 0; n < NTD; ++n)
+        for (int n = 0; n < NTD; ++n) {
+          // a d tile's 32 values loaded together, then added (added as each
+          // arrived, the loads went out one at a time)
+          float tk[16], tv[16];
 #pragma unroll
           for (int a = 0; a < 16; ++a) {
-            dk[n][a] += load_coherent(pp + (n * 16 + a) * 64);
-            dv[n][a] += load_coherent(pp + ((NTD + n) * 16 + a) * 64);
+            tk[a] = load_coherent(pp + (n * 16 + a) * 64);
+            tv[a] = load_coherent(pp + ((NTD + n) * 16 + a) * 64);
           }
+#pragma unroll
+          for (int a = 0; a < 16; ++a) {
+            dk[n][a] += tk[a];
+            dv[n][a] += tv[a];
+          }
+        }
       }
     }
   }
@@ -820,9 +829,13 @@ __global__ __launch_bounds__(NT, kDqBlocksPerCu<D>) void bwd_dq_db_kernel(const 
     for (int sl = s0; sl < s0 + ns; ++sl) {
       const float* po = part(sl);
 #pragma unroll
-      for (int n = 0; n < NTD; ++n)
+      for (int n = 0; n < NTD; ++n) {
+        float t[16];  // loaded together, then added
 #pragma unroll
-        for (int a = 0; a < 16; ++a) dq[n][a] += load_coherent(po + (16 * n + a) * NT);
+        for (int a = 0; a < 16; ++a) t[a] = load_coherent(po + (16 * n + a) * NT);
+#pragma unroll
+        for (int a = 0; a < 16; ++a) dq[n][a] += t[a];
+      }
     }
   }
 
