@@ -309,8 +309,8 @@ bsattn_status bsattn_prefill_fwd(const bsattn_prefill_args* args, void* stream);
  * fp32 partial sums to the workspace; the last chunk of an item to arrive
  * adds them in slot order and writes the gradient, so the results stay
  * deterministic (they differ from an uncut run only in the order of fp32
- * additions).  Plus a small clear of the arrival counters when a schedule
- * cuts anything.  No float atomics.
+ * additions).  The rowsum launch also zeroes the arrival counters that a
+ * cutting schedule counts with.  No float atomics.
  */
 typedef struct {
   int32_t dtype;          /* BSATTN_BF16 */
