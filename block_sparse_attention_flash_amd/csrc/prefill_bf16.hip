@@ -468,7 +468,14 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     // long arrived; saying so (through the builtin the compiler tracks) keeps
     // its scalar load from coarsening the K-fragment waits below
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    if (it + ST - 1 < nblk) fetch(it + ST - 1, ST == 3 ? q2 : q1);
+    // The next stage's loads: here in the static kernels; with the vote,
+    // after it (below), so that their LDS writes land under the
+    // exponentials and P.V instead of under the QK^T reads and the vote's
+    // polls (measured: the causal GQA 32K launch 1-1.7 % faster, its sink
+    // recipe 1.5-2.5 %; the same placement 0.5 % slower on the static video
+    // mask).
+    const int jf = ST == 3 ? q2 : q1;
+    if (!DYN && it + ST - 1 < nblk) fetch(it + ST - 1, jf);
     q0 = q1;
     q1 = q2;
     if constexpr (ST == 3) q2 = q3;
@@ -530,6 +537,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
     }
     const float mb = wave_max_xor32(fmaxf(mb0, mb1));
     if constexpr (MAXONLY) {
+      if (it + ST - 1 < nblk) fetch(it + ST - 1, jf);
       m_chunk = fmaxf(m_chunk, mb);
       if constexpr (ST == 3) q3 = blk(it + 4);
       else q2 = blk(it + 3);
@@ -569,6 +577,7 @@ __global__ __launch_bounds__(NT, kMinBlocksPerCu<D>) void prefill_bf16_kernel(co
         }
       }
     }
+    if (DYN && it + ST - 1 < nblk) fetch(it + ST - 1, jf);
     if (p.block_state && tid == 0)
       p.block_state[(((int64_t)b * p.Hq + h) * p.Tr + t) * p.Tc + j] = skip ? 2 : 1;
     m_run = m_new;
