@@ -196,8 +196,8 @@ struct DkdvSmem {
   __bf16 v[NB][BC * D];
   __bf16 q[2][64 * D];  // double-buffered 64-row query stages
   __bf16 g[2][64 * D];  // their dout
-  float lse[2][64];     // per stage: lse (natural log) and Dv of its rows
-  float dvec[2][64];
+  alignas(16) float lse[2][64];  // per stage: lse (natural log) and Dv of its rows
+  alignas(16) float dvec[2][64];
   int ticket;           // a chunk's arrival ticket (after the reduction, which overlays the tiles)
 };
 
@@ -462,9 +462,14 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
     step(nxt);
     int t_nxt = 0, need_nxt = 0;
     const bool have_nxt = settle(nxt, t_nxt, need_nxt);
-    if (have_nxt) fetch(buf ^ 1, g * G + nxt.hc, t_nxt, nxt.hf);
+    // the next stage's loads: after this stage's S and dP products, so that
+    // their LDS writes do not land under those products' fragment reads (at
+    // once in waves whose block sits this stage out; every wave loads its
+    // share of the stage)
+    const bool mine = (need >> kb) & 1;
+    if (!mine && have_nxt) fetch(buf ^ 1, g * G + nxt.hc, t_nxt, nxt.hf);
 
-    if ((need >> kb) & 1) {
+    if (mine) {
       const int row0 = t * BR + 64 * hf;
       const int nrows = min(64, p.Nq - row0);
       const int r0 = 32 * qh;
@@ -495,25 +500,38 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (have_nxt) fetch(buf ^ 1, g * G + nxt.hc, t_nxt, nxt.hf);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         // P and dS of this lane's 8 (row, key) pairs of the key step: rows
         // r0 + 16 kk + 8 q + 4 hi + (0..3), q = 0, 1, whose lse and Dv come in
         // four-row vector reads; masked pairs take 0 by a select (no branch)
+        // (read in an asm block and waited for in it: read plainly, the
+        // compiler first waited for the next stage's global->LDS loads, as it
+        // cannot tell the stage read from the stage being filled.  The S and
+        // dP accumulators stay live, so no output lands on an in-flight
+        // product's accumulator.)
+        f32x4 l4[2], d4[2];
+        asm volatile(
+            "ds_read_b128 %0, %4\n"
+            "ds_read_b128 %1, %4 offset:32\n"
+            "ds_read_b128 %2, %5\n"
+            "ds_read_b128 %3, %5 offset:32\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(l4[0]), "=&v"(l4[1]), "=&v"(d4[0]), "=&v"(d4[1])
+            : "v"(lds_addr_b(sm.lse[buf] + r0 + 16 * kk + 4 * hi)), "v"(lds_addr_b(sm.dvec[buf] + r0 + 16 * kk + 4 * hi))
+            : "memory");
         float pv[8], dsv[8];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int rb = r0 + 16 * kk + 8 * q + 4 * hi;
-          const float4 l4 = *reinterpret_cast<const float4*>(sm.lse[buf] + rb);
-          const float4 d4 = *reinterpret_cast<const float4*>(sm.dvec[buf] + rb);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int i = 4 * q + u, a = 8 * kk + i, rl = rb + u;
             const bool ok = key_ok && rl < nrows && (!CAUSAL || key <= row0 + rl);
-            const float e = fast_exp2(fmaf(s[a], c2, -lv[u] * kLog2e));
+            const float e = fast_exp2(fmaf(s[a], c2, -l4[q][u] * kLog2e));
             pv[i] = ok ? e : 0.0f;
-            dsv[i] = pv[i] * (dp[a] - dvv[u]);
+            dsv[i] = pv[i] * (dp[a] - d4[q][u]);
           }
         }
         const bf16x8 pb = to_bf16x8(pv);
