@@ -503,14 +503,14 @@ __global__ __launch_bounds__(256 * kDkdvBlocks<D>, kDkdvBlocks<D> * kDkdvGroupsP
       if (have_nxt) fetch(buf ^ 1, g * G + nxt.hc, t_nxt, nxt.hf);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        // P and dS of this lane's 8 (row, key) pairs of the key step: rows
-        // r0 + 16 kk + 8 q + 4 hi + (0..3), q = 0, 1, whose lse and Dv come in
-        // four-row vector reads; masked pairs take 0 by a select (no branch)
-        // (read in an asm block and waited for in it: read plainly, the
-        // compiler first waited for the next stage's global->LDS loads, as it
-        // cannot tell the stage read from the stage being filled.  The S and
+        // P and dS of this lane's 8 (row, key) pairs of the key step, rows
+        // r0 + 16 kk + 8 q + 4 hi + (0..3), q = 0, 1; masked pairs take 0 by a
+        // select (no branch).  The rows' lse and Dv come in four-row reads
+        // issued and waited for in one asm block: read plainly, they made the
+        // compiler wait first for the next stage's global->LDS loads (it
+        // cannot tell the stage read from the stage being filled).  The S and
         // dP accumulators stay live, so no output lands on an in-flight
-        // product's accumulator.)
+        // product's accumulator.
         f32x4 l4[2], d4[2];
         asm volatile(
             "ds_read_b128 %0, %4\n"
