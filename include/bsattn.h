@@ -348,7 +348,10 @@ typedef struct {
                              lambda > 0 wrote; blocks it skipped (2) get no gradient, so the
                              gradients are those of the function that forward computed (softmax
                              over its kept blocks; BLASST notes, training with the skipping
-                             forward).  NULL = every visited block */
+                             forward).  Read through the scalar cache in aligned 4-byte words,
+                             so the up to 3 bytes beside the array in its first and last words
+                             are read and ignored (never past a page the array touches).
+                             NULL = every visited block */
   const int32_t* dq_items;  /* optional device copy of bsattn_build_schedule's items for the CSR
                                (needs it); NULL = one dq work-group per tile, and the four dq_
                                counts / merges below must be 0 / NULL */
